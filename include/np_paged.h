@@ -1,0 +1,215 @@
+/*
+ * np_paged.h -- C ABI of the paged-attention library for AMD MI355X (gfx950).
+ *
+ * The library computes, for every sequence s, query row i and query head h,
+ *
+ *     out[s,i,h,:] = sum_t softmax_t(scale * <q[s,i,h,:], K_s[t]>) * V_s[t]
+ *
+ * over the keys t <= past_s + i of KV head h / (Hq / Hkv), where K_s[t] and
+ * V_s[t] are read through the sequence's block table from a pool of
+ * fixed-size physical blocks. Sources, by page title and section:
+ *
+ *   - "I Wrote the Three Attention Kernels That Run LLM Inference -- in
+ *     Portable Triton, on a Free Colab T4": "What is attention, really?"
+ *     (the definition), "3. Paged KV-cache attention" (page lookup through
+ *     the block table; GQA-aware), "2. Split-KV flash-decoding" (splitting the
+ *     KV range across workgroups and merging the splits by log-sum-exp).
+ *   - "Day 23: the real triton.jit paged-attention kernel": "What I added
+ *     today" (every integer that becomes a pointer -- slot stride, past, grid,
+ *     padded tile sizes -- is computed by plain host code that is tested
+ *     without a GPU) and "What I learned", item 1 (pad head_dim to a power of
+ *     two and mask the lanes past the real extent, as for the ragged tail).
+ *
+ * Layout (all strides in ELEMENTS; the last dimension of every tensor is
+ * contiguous):
+ *   q            [n_q_total, Hq, head_dim]        strides q_stride[0..1]
+ *   k_pool/v_pool[n_blocks, block_size, Hkv, d]   strides kv_stride[0..2]
+ *   out          [n_q_total, Hq, head_dim]        strides out_stride[0..1]
+ *   block_table  int32 [num_seqs, max_blocks_per_seq], row stride bt_stride
+ *   context_lens int32 [num_seqs]  -- cached tokens INCLUDING the current
+ *                query tokens, whose K/V are already in the pool
+ *   q_start      int32 [num_seqs + 1] (prefill only) -- rows of sequence s
+ *                are q_start[s] .. q_start[s+1]-1; past_s = context_lens[s]
+ *                - (q_start[s+1] - q_start[s]).
+ * Token t of sequence s lives in slot t % block_size of physical block
+ * block_table[s, t / block_size].
+ *
+ * Ownership: every device buffer is allocated by the caller. A plan is owned
+ * by the library, created by np_plan and released by np_plan_destroy. The
+ * library keeps no mutable global state; all calls are reentrant.
+ *
+ * Errors: every function returns an np_status; nothing throws or aborts
+ * across this ABI. Device-side block-table entries and context lengths that
+ * disagree with what the host validated are undefined behaviour (the kernels
+ * clamp table reads to the table's width but not entry values to the pool).
+ */
+#ifndef NP_PAGED_H
+#define NP_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum np_dtype { NP_F32 = 0, NP_F16 = 1, NP_BF16 = 2 } np_dtype;
+
+typedef enum np_status {
+  NP_OK = 0,
+  NP_ERR_NULL_PTR = 1,        /* a required pointer is NULL                    */
+  NP_ERR_BAD_DTYPE = 2,       /* dtype not one of np_dtype                     */
+  NP_ERR_BAD_SHAPE = 3,       /* a size is < 1, block_size not a power of two,
+                                 or q rows do not match the sequences          */
+  NP_ERR_BAD_STRIDE = 4,      /* a stride is too small (rows would overlap)    */
+  NP_ERR_MISALIGNED = 5,      /* a pointer or row is not 16-byte aligned       */
+  NP_ERR_BAD_GQA = 6,         /* Hq is not a multiple of Hkv                   */
+  NP_ERR_BAD_CONTEXT_LEN = 7, /* context_len < query rows or > table capacity  */
+  NP_ERR_BAD_BLOCK_TABLE = 8, /* a used table entry is outside [0, n_blocks)   */
+  NP_ERR_UNSUPPORTED = 9,     /* valid, but no kernel is built for this shape  */
+  NP_ERR_WORKSPACE_TOO_SMALL = 10,
+  NP_ERR_BAD_PLAN = 11,       /* plan missing or made for another descriptor   */
+  NP_ERR_HIP = 12             /* a HIP launch reported an error                */
+} np_status;
+
+/* Shape and stride descriptor shared by every call. */
+typedef struct np_paged_desc {
+  int32_t dtype;              /* np_dtype of q, the pools and out              */
+  int32_t num_seqs;
+  int32_t n_q_total;          /* query rows: num_seqs for decode               */
+  int32_t num_q_heads;        /* Hq                                            */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0                            */
+  int32_t head_dim;           /* d                                             */
+  int32_t block_size;         /* slots per physical block, power of two        */
+  int32_t n_blocks;           /* physical blocks in each pool                  */
+  int32_t max_blocks_per_seq; /* block-table width                             */
+  int32_t reserved0;          /* must be 0                                     */
+  int64_t q_stride[2];        /* [row, head]                                   */
+  int64_t kv_stride[3];       /* [block, slot, head]; same for K and V         */
+  int64_t out_stride[2];      /* [row, head]                                   */
+  int64_t bt_stride;          /* block-table row stride                        */
+  float scale;                /* <= 0 selects 1/sqrt(head_dim)                 */
+  int32_t reserved1;          /* must be 0                                     */
+} np_paged_desc;
+
+/* Planner knobs; pass NULL for the defaults. */
+typedef struct np_plan_opts {
+  int32_t num_cus;                /* compute units to fill; 0 => 256           */
+  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 2          */
+  int32_t min_blocks_per_split;   /* 0 => 4                                    */
+  int32_t max_blocks_per_split;   /* 0 => 1024 tokens' worth of blocks         */
+  int32_t force_blocks_per_split; /* > 0: use exactly this split size          */
+  int32_t reserved;               /* must be 0                                 */
+} np_plan_opts;
+
+typedef struct np_plan_s np_plan_t;   /* opaque, host memory only */
+
+/*
+ * np_check_paged_inputs -- validate a call without touching the GPU.
+ *
+ * Checks the descriptor, the device pointers (non-NULL, 16-byte aligned for
+ * q/pools/out, 4-byte for int32 arrays), strides and GQA divisibility. When
+ * the host copies are given it also checks 1 <= n_q_s <= context_lens[s] <=
+ * max_blocks_per_seq * block_size (with q_start_host for prefill; decode has
+ * one row per sequence) and that every used table entry, columns 0 ..
+ * ceil(context_lens[s] / block_size) - 1, lies in [0, n_blocks). Host arrays
+ * may be NULL to skip those checks. Returns the first error found.
+ */
+np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_table,
+                                const int32_t* context_lens, const void* out,
+                                const int32_t* block_table_host,
+                                const int32_t* context_lens_host,
+                                const int32_t* q_start_host);
+
+/*
+ * np_plan -- plan the split-KV decode or the chunked prefill for one batch.
+ *
+ * Pure host code, deterministic: the same inputs give the same plan bit for
+ * bit. context_lens_host [num_seqs] is required. q_start_host NULL makes a
+ * decode plan (one query row per sequence); otherwise a prefill plan.
+ *
+ * Decode: every sequence's ceil(L/block_size) logical blocks are cut into
+ * splits of `blocks_per_split` consecutive blocks (the last may be shorter,
+ * none is empty), one workgroup per (sequence, KV head, split), following the
+ * split-KV partition of "2. Split-KV flash-decoding" with page-aligned,
+ * never-empty splits. blocks_per_split = clamp(ceil(total_blocks * Hkv /
+ * (num_cus * wgs_per_cu)), min, max), or the forced value.
+ * Prefill: one workgroup per (sequence, KV head, tile of query rows).
+ *
+ * On success *out owns a new plan; the caller releases it with
+ * np_plan_destroy after the last launch that uses it.
+ */
+np_status np_plan(const np_paged_desc* desc, const int32_t* context_lens_host,
+                  const int32_t* q_start_host, const np_plan_opts* opts,
+                  np_plan_t** out);
+
+void np_plan_destroy(np_plan_t* plan);
+
+/* Device workspace bytes the plan's launches need (0 if none). */
+size_t np_plan_workspace_bytes(const np_plan_t* plan);
+
+/* Read-only plan accessors (for tests and the benchmark). */
+int32_t np_plan_blocks_per_split(const np_plan_t* plan);
+int32_t np_plan_max_splits(const np_plan_t* plan);
+int32_t np_plan_is_prefill(const np_plan_t* plan);
+int64_t np_plan_num_work_items(const np_plan_t* plan);
+/* item[0..4] = sequence, kv head, split (or query tile), first block (or
+ * first query row, relative to the sequence), end block (or end row).
+ * Items are listed in launch order of the active workgroups. */
+np_status np_plan_work_item(const np_plan_t* plan, int64_t index, int32_t item[5]);
+/* grid[0..2] and the workgroup size of the main kernel; *combine_wgs is the
+ * number of workgroups of the split-combine kernel (0 if no split). */
+np_status np_plan_launch_shape(const np_plan_t* plan, uint32_t grid[3],
+                               uint32_t* wg_size, uint32_t* combine_wgs);
+
+/* Host-side helper exposed for tests: smallest power of two >= x (x >= 1). */
+int32_t np_next_pow2(int32_t x);
+
+/*
+ * np_paged_attention_decode -- one query token per sequence.
+ *
+ * q/out [num_seqs, Hq, d]. Launches the split-KV decode kernel and, when any
+ * sequence has more than one split, the combine kernel, asynchronously on
+ * `stream` (a hipStream_t; NULL = the null stream). Never allocates, never
+ * synchronises. `workspace` (device, 256-byte aligned) must hold
+ * np_plan_workspace_bytes(plan) bytes; its contents need not be initialised
+ * and are scratch after the call. Checks the descriptor and pointers (not
+ * the device arrays' values) and that the plan was made for this descriptor.
+ * Built kernels: block_size 16; head_dim a multiple of 8 (16-bit types) or 4
+ * (fp32) up to 128; Hq/Hkv from 1 to 8. Other valid shapes return
+ * NP_ERR_UNSUPPORTED.
+ */
+np_status np_paged_attention_decode(const np_paged_desc* desc, const np_plan_t* plan,
+                                    const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_table,
+                                    const int32_t* context_lens, void* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * np_paged_attention_prefill -- a chunk of n_q_s new query rows per sequence,
+ * causal: row i of sequence s sees keys t <= past_s + i ("Day 23", "What I
+ * added today": past is computed on the host side of the interface; here the
+ * kernel derives it from context_lens and q_start exactly as stated above).
+ * QK^T and PV run on the MFMA units in bf16/fp16 with fp32 accumulation.
+ * Built kernels: bf16 and fp16, head_dim 64, block_size 16, Hq/Hkv 1..8.
+ * q_start is a device array [num_seqs + 1]. Same stream, allocation and
+ * error rules as decode.
+ */
+np_status np_paged_attention_prefill(const np_paged_desc* desc, const np_plan_t* plan,
+                                     const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table,
+                                     const int32_t* context_lens, const int32_t* q_start,
+                                     void* out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* np_status_string(np_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NP_PAGED_H */

@@ -1,0 +1,74 @@
+"""Build the HIP library ``libnp_paged.so`` in-tree for gfx950.
+
+The host half (checks, planner) is compiled with g++ to keep it free of HIP;
+the kernels and launchers with hipcc. All device code is built with packed
+fp32 instructions disabled.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libnp_paged.so")
+
+HIP_SOURCES = ["np_decode.hip", "np_prefill.hip"]
+HOST_SOURCES = ["np_host.cpp"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP library cannot be built")
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    return res
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link ``libnp_paged.so``; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    incs = ["-I", INCLUDE, "-I", CSRC]
+    steps = []
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        steps.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *incs, "-c",
+                      os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        steps.append([hipcc, *HIPCC_FLAGS, *incs, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(steps)))) as ex:
+        for res in ex.map(_run, steps):
+            if verbose and (res.stdout or res.stderr):
+                sys.stderr.write(res.stdout + res.stderr)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

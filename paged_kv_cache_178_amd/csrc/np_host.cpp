@@ -1,0 +1,333 @@
+// Host half of the library: input checks and the split/grid planner.
+//
+// Plain C++17 with no HIP dependency, so every integer the kernels turn into
+// a pointer or a loop bound is produced and tested without a GPU ("Day 23:
+// the real triton.jit paged-attention kernel", section "What I added today").
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <new>
+
+#include "np_internal.h"
+
+namespace np {
+
+size_t dtype_size(int32_t dtype) {
+  switch (dtype) {
+    case NP_F32: return 4;
+    case NP_F16: return 2;
+    case NP_BF16: return 2;
+    default: return 0;
+  }
+}
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+np_status check_desc(const np_paged_desc* d) {
+  if (d == nullptr) return NP_ERR_NULL_PTR;
+  if (dtype_size(d->dtype) == 0) return NP_ERR_BAD_DTYPE;
+  if (d->num_seqs < 1 || d->n_q_total < d->num_seqs || d->num_q_heads < 1 ||
+      d->num_kv_heads < 1 || d->head_dim < 1 || d->n_blocks < 1 ||
+      d->max_blocks_per_seq < 1 || d->reserved0 != 0 || d->reserved1 != 0)
+    return NP_ERR_BAD_SHAPE;
+  if (!is_pow2(d->block_size) || d->block_size > 256) return NP_ERR_BAD_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return NP_ERR_BAD_GQA;
+  if (!(d->scale <= 0.0f || std::isfinite(d->scale))) return NP_ERR_BAD_SHAPE;
+  const int64_t hd = d->head_dim;
+  // Rows must not overlap: each stride covers the extent of the dimension below.
+  if (d->q_stride[1] < hd || d->q_stride[0] < (d->num_q_heads - 1) * d->q_stride[1] + hd)
+    return NP_ERR_BAD_STRIDE;
+  if (d->out_stride[1] < hd ||
+      d->out_stride[0] < (d->num_q_heads - 1) * d->out_stride[1] + hd)
+    return NP_ERR_BAD_STRIDE;
+  if (d->kv_stride[2] < hd ||
+      d->kv_stride[1] < (d->num_kv_heads - 1) * d->kv_stride[2] + hd ||
+      d->kv_stride[0] < (d->block_size - 1) * d->kv_stride[1] +
+                            (d->num_kv_heads - 1) * d->kv_stride[2] + hd)
+    return NP_ERR_BAD_STRIDE;
+  if (d->bt_stride < d->max_blocks_per_seq) return NP_ERR_BAD_STRIDE;
+  // Every row starts on a 16-byte boundary so the kernels can use 128-bit loads.
+  const int64_t elt = static_cast<int64_t>(dtype_size(d->dtype));
+  const int64_t strides[] = {d->q_stride[0], d->q_stride[1], d->kv_stride[0],
+                             d->kv_stride[1], d->kv_stride[2], d->out_stride[0],
+                             d->out_stride[1]};
+  for (int64_t s : strides)
+    if ((s * elt) % 16 != 0) return NP_ERR_MISALIGNED;
+  if ((hd * elt) % 16 != 0) return NP_ERR_MISALIGNED;
+  return NP_OK;
+}
+
+np_status check_pointers(const np_paged_desc* d, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table,
+                         const int32_t* context_lens, const void* out) {
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
+    return NP_ERR_NULL_PTR;
+  (void)d;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
+    return NP_ERR_MISALIGNED;
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4)) return NP_ERR_MISALIGNED;
+  return NP_OK;
+}
+
+np_status check_plan(const np_paged_desc* d, const np_plan_t* plan, int want_prefill) {
+  if (plan == nullptr || plan->magic != kPlanMagic) return NP_ERR_BAD_PLAN;
+  const np_plan_core& c = plan->core;
+  if (c.is_prefill != want_prefill || c.dtype != d->dtype || c.num_seqs != d->num_seqs ||
+      c.n_q_total != d->n_q_total || c.hq != d->num_q_heads || c.hkv != d->num_kv_heads ||
+      c.head_dim != d->head_dim || c.block_size != d->block_size ||
+      c.max_blocks != d->max_blocks_per_seq)
+    return NP_ERR_BAD_PLAN;
+  return NP_OK;
+}
+
+static np_status check_host_arrays(const np_paged_desc* d, const int32_t* lens,
+                                   const int32_t* q_start, const int32_t* table) {
+  if (lens == nullptr) return NP_OK;
+  const int64_t cap = static_cast<int64_t>(d->max_blocks_per_seq) * d->block_size;
+  if (q_start == nullptr) {
+    if (d->n_q_total != d->num_seqs) return NP_ERR_BAD_SHAPE;
+  } else {
+    if (q_start[0] != 0 || q_start[d->num_seqs] != d->n_q_total) return NP_ERR_BAD_SHAPE;
+  }
+  for (int32_t s = 0; s < d->num_seqs; ++s) {
+    const int64_t n_q = q_start ? int64_t(q_start[s + 1]) - q_start[s] : 1;
+    if (n_q < 1) return NP_ERR_BAD_SHAPE;
+    if (lens[s] < n_q || lens[s] > cap) return NP_ERR_BAD_CONTEXT_LEN;
+  }
+  if (table == nullptr) return NP_OK;
+  for (int32_t s = 0; s < d->num_seqs; ++s) {
+    const int64_t used = ceil_div(lens[s], d->block_size);
+    const int32_t* row = table + static_cast<int64_t>(s) * d->bt_stride;
+    for (int64_t j = 0; j < used; ++j)
+      if (row[j] < 0 || row[j] >= d->n_blocks) return NP_ERR_BAD_BLOCK_TABLE;
+  }
+  return NP_OK;
+}
+
+}  // namespace np
+
+using namespace np;
+
+extern "C" {
+
+int32_t np_next_pow2(int32_t x) {
+  if (x <= 1) return 1;
+  int32_t p = 1;
+  while (p < x && p < (1 << 30)) p <<= 1;
+  return p;
+}
+
+const char* np_status_string(np_status s) {
+  switch (s) {
+    case NP_OK: return "ok";
+    case NP_ERR_NULL_PTR: return "null pointer";
+    case NP_ERR_BAD_DTYPE: return "bad dtype";
+    case NP_ERR_BAD_SHAPE: return "bad shape";
+    case NP_ERR_BAD_STRIDE: return "bad stride";
+    case NP_ERR_MISALIGNED: return "misaligned pointer or row";
+    case NP_ERR_BAD_GQA: return "num_q_heads is not a multiple of num_kv_heads";
+    case NP_ERR_BAD_CONTEXT_LEN: return "bad context length";
+    case NP_ERR_BAD_BLOCK_TABLE: return "block table entry out of range";
+    case NP_ERR_UNSUPPORTED: return "shape valid but no kernel built for it";
+    case NP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case NP_ERR_BAD_PLAN: return "plan missing or made for another descriptor";
+    case NP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                const void* out, const int32_t* block_table_host,
+                                const int32_t* context_lens_host,
+                                const int32_t* q_start_host) {
+  np_status st = check_desc(desc);
+  if (st != NP_OK) return st;
+  st = check_pointers(desc, q, k_pool, v_pool, block_table, context_lens, out);
+  if (st != NP_OK) return st;
+  return check_host_arrays(desc, context_lens_host, q_start_host, block_table_host);
+}
+
+np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t* q_start,
+                  const np_plan_opts* opts, np_plan_t** out) {
+  if (out == nullptr || lens == nullptr) return NP_ERR_NULL_PTR;
+  *out = nullptr;
+  np_status st = check_desc(desc);
+  if (st != NP_OK) return st;
+  st = check_host_arrays(desc, lens, q_start, nullptr);
+  if (st != NP_OK) return st;
+  np_plan_opts o{};
+  if (opts) o = *opts;
+  if (o.reserved != 0 || o.num_cus < 0 || o.wgs_per_cu < 0 || o.min_blocks_per_split < 0 ||
+      o.max_blocks_per_split < 0 || o.force_blocks_per_split < 0)
+    return NP_ERR_BAD_SHAPE;
+  const int32_t num_cus = o.num_cus ? o.num_cus : 256;
+  const int32_t wgs_per_cu = o.wgs_per_cu ? o.wgs_per_cu : 2;
+  const int32_t min_bps = o.min_blocks_per_split ? o.min_blocks_per_split : 4;
+  const int32_t max_bps = o.max_blocks_per_split
+                              ? o.max_blocks_per_split
+                              : std::max<int32_t>(1, 1024 / desc->block_size);
+
+  np_plan_s* plan = new (std::nothrow) np_plan_s();
+  if (plan == nullptr) return NP_ERR_UNSUPPORTED;
+  plan->magic = kPlanMagic;
+  np_plan_core& c = plan->core;
+  c.dtype = desc->dtype;
+  c.num_seqs = desc->num_seqs;
+  c.n_q_total = desc->n_q_total;
+  c.hq = desc->num_q_heads;
+  c.hkv = desc->num_kv_heads;
+  c.head_dim = desc->head_dim;
+  c.block_size = desc->block_size;
+  c.max_blocks = desc->max_blocks_per_seq;
+  c.group = c.hq / c.hkv;
+  c.d_pad = np_next_pow2(c.head_dim);
+  c.is_prefill = q_start != nullptr;
+
+  if (!c.is_prefill) {
+    // Split-KV decode ("2. Split-KV flash-decoding"): page-aligned splits of a
+    // uniform number of blocks, so that no split is empty and each workgroup
+    // streams at most blocks_per_split blocks.
+    int64_t total_blocks = 0;
+    int64_t max_nb = 0;
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t nb = ceil_div(lens[s], c.block_size);
+      total_blocks += nb;
+      max_nb = std::max(max_nb, nb);
+    }
+    int64_t bps;
+    if (o.force_blocks_per_split > 0) {
+      bps = o.force_blocks_per_split;
+    } else {
+      const int64_t target_wgs = int64_t(num_cus) * wgs_per_cu;
+      bps = ceil_div(total_blocks * c.hkv, target_wgs);
+      bps = std::max<int64_t>(bps, min_bps);
+      bps = std::min<int64_t>(bps, std::max(max_bps, min_bps));
+    }
+    bps = std::min<int64_t>(bps, std::max<int64_t>(max_nb, 1));
+    c.blocks_per_split = static_cast<int32_t>(bps);
+    c.max_splits = static_cast<int32_t>(ceil_div(max_nb, bps));
+    c.max_tiles = 0;
+    c.grid[0] = static_cast<uint32_t>(int64_t(c.max_splits) * c.hkv);
+    c.grid[1] = static_cast<uint32_t>(c.num_seqs);
+    c.grid[2] = 1;
+    c.wg_size = kDecodeWaves * kWaveSize;
+    bool any_split = false;
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t splits = ceil_div(ceil_div(lens[s], c.block_size), bps);
+      any_split = any_split || splits > 1;
+      for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
+        const int64_t split = x / c.hkv, kvh = x % c.hkv;
+        if (split >= splits) continue;
+        const int64_t b0 = split * bps;
+        const int64_t b1 = std::min<int64_t>(b0 + bps, ceil_div(lens[s], c.block_size));
+        const int32_t item[5] = {s, int32_t(kvh), int32_t(split), int32_t(b0), int32_t(b1)};
+        plan->items.insert(plan->items.end(), item, item + 5);
+      }
+    }
+    c.combine_wgs = any_split ? static_cast<uint32_t>(c.num_seqs * c.hkv) : 0;
+    if (any_split) {
+      const size_t n_part = size_t(c.num_seqs) * c.hq * c.max_splits;
+      c.ws_ml_off = 0;
+      const size_t ml_bytes = (n_part * 2 * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+      c.ws_acc_off = ml_bytes;
+      const size_t acc_bytes =
+          (n_part * c.d_pad * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+      c.ws_bytes = ml_bytes + acc_bytes;
+    } else {
+      c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
+    }
+  } else {
+    // Chunked prefill: one workgroup per (sequence, KV head, tile). A tile is
+    // kPrefillWaves units; a unit is one query head of the group times
+    // kPrefillRowsPerWave query rows. Units are numbered head-fastest.
+    int64_t max_tiles = 0;
+    std::vector<int64_t> tiles(c.num_seqs);
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
+      const int64_t units = c.group * ceil_div(n_q, kPrefillRowsPerWave);
+      tiles[s] = ceil_div(units, kPrefillWaves);
+      max_tiles = std::max(max_tiles, tiles[s]);
+    }
+    c.blocks_per_split = 0;
+    c.max_splits = 1;
+    c.max_tiles = static_cast<int32_t>(max_tiles);
+    c.grid[0] = static_cast<uint32_t>(max_tiles * c.hkv);
+    c.grid[1] = static_cast<uint32_t>(c.num_seqs);
+    c.grid[2] = 1;
+    c.wg_size = kPrefillWaves * kWaveSize;
+    c.combine_wgs = 0;
+    c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
+      for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
+        const int64_t tile = x / c.hkv, kvh = x % c.hkv;
+        if (tile >= tiles[s]) continue;
+        // Rows covered by the tile's units (clipped to the chunk).
+        const int64_t u0 = tile * kPrefillWaves;
+        const int64_t u1 = std::min<int64_t>(u0 + kPrefillWaves,
+                                             c.group * ceil_div(n_q, kPrefillRowsPerWave));
+        const int64_t r0 = (u0 / c.group) * kPrefillRowsPerWave;
+        const int64_t r1 = std::min<int64_t>(((u1 - 1) / c.group + 1) * kPrefillRowsPerWave, n_q);
+        const int32_t item[5] = {s, int32_t(kvh), int32_t(tile), int32_t(r0), int32_t(r1)};
+        plan->items.insert(plan->items.end(), item, item + 5);
+      }
+    }
+  }
+  *out = plan;
+  return NP_OK;
+}
+
+void np_plan_destroy(np_plan_t* plan) {
+  if (plan && plan->magic == kPlanMagic) {
+    plan->magic = 0;
+    delete plan;
+  }
+}
+
+size_t np_plan_workspace_bytes(const np_plan_t* p) {
+  return (p && p->magic == kPlanMagic) ? p->core.ws_bytes : 0;
+}
+
+int32_t np_plan_blocks_per_split(const np_plan_t* p) {
+  return (p && p->magic == kPlanMagic) ? p->core.blocks_per_split : -1;
+}
+
+int32_t np_plan_max_splits(const np_plan_t* p) {
+  return (p && p->magic == kPlanMagic) ? p->core.max_splits : -1;
+}
+
+int32_t np_plan_is_prefill(const np_plan_t* p) {
+  return (p && p->magic == kPlanMagic) ? p->core.is_prefill : -1;
+}
+
+int64_t np_plan_num_work_items(const np_plan_t* p) {
+  return (p && p->magic == kPlanMagic) ? int64_t(p->items.size() / 5) : -1;
+}
+
+np_status np_plan_work_item(const np_plan_t* p, int64_t index, int32_t item[5]) {
+  if (p == nullptr || p->magic != kPlanMagic || item == nullptr) return NP_ERR_NULL_PTR;
+  if (index < 0 || index >= int64_t(p->items.size() / 5)) return NP_ERR_BAD_SHAPE;
+  std::memcpy(item, p->items.data() + index * 5, 5 * sizeof(int32_t));
+  return NP_OK;
+}
+
+np_status np_plan_launch_shape(const np_plan_t* p, uint32_t grid[3], uint32_t* wg_size,
+                               uint32_t* combine_wgs) {
+  if (p == nullptr || p->magic != kPlanMagic) return NP_ERR_BAD_PLAN;
+  if (grid) std::memcpy(grid, p->core.grid, sizeof(p->core.grid));
+  if (wg_size) *wg_size = p->core.wg_size;
+  if (combine_wgs) *combine_wgs = p->core.combine_wgs;
+  return NP_OK;
+}
+
+}  // extern "C"

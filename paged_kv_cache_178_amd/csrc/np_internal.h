@@ -1,0 +1,61 @@
+// Internal declarations shared by the host code (np_host.cpp, plain C++) and
+// the HIP launch code. No HIP headers here: the host half builds with g++.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "np_paged.h"
+
+namespace np {
+
+constexpr uint32_t kPlanMagic = 0x4e50504cu;   // "NPPL"
+constexpr int kWaveSize = 64;
+constexpr int kDecodeWaves = 4;                // waves per decode workgroup
+constexpr int kPrefillWaves = 4;               // waves per prefill workgroup
+constexpr int kPrefillRowsPerWave = 32;        // query rows of one head per wave
+constexpr int kMaxGroup = 8;                   // largest Hq/Hkv with a kernel
+constexpr size_t kWsAlign = 256;
+
+// Sizes every launch depends on, fixed when the plan is made.
+struct np_plan_core {
+  int32_t dtype, num_seqs, n_q_total, hq, hkv, head_dim, block_size, max_blocks;
+  int32_t group;           // Hq / Hkv
+  int32_t d_pad;           // next power of two >= head_dim
+  int32_t is_prefill;
+  // decode
+  int32_t blocks_per_split;
+  int32_t max_splits;      // over sequences
+  // prefill
+  int32_t max_tiles;       // workgroup tiles per (sequence, KV head), max over sequences
+  // launch
+  uint32_t grid[3];
+  uint32_t wg_size;
+  uint32_t combine_wgs;
+  // workspace (bytes from the workspace base)
+  size_t ws_ml_off;        // float2 (m, l) [num_seqs][Hq][max_splits]
+  size_t ws_acc_off;       // float [num_seqs][Hq][max_splits][d_pad]
+  size_t ws_bytes;
+};
+
+}  // namespace np
+
+struct np_plan_s {
+  uint32_t magic;
+  np::np_plan_core core;
+  std::vector<int32_t> items;   // 5 ints per active workgroup, launch order
+};
+
+namespace np {
+
+// Descriptor-level checks shared by np_check_paged_inputs and the launchers.
+np_status check_desc(const np_paged_desc* d);
+np_status check_pointers(const np_paged_desc* d, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table,
+                         const int32_t* context_lens, const void* out);
+// The plan was made for this descriptor.
+np_status check_plan(const np_paged_desc* d, const np_plan_t* plan, int want_prefill);
+size_t dtype_size(int32_t dtype);
+
+}  // namespace np
