@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+Workload: Llama-3.2-1B head shape (Hq=32, Hkv=8, d=64), block size 16, one
+sequence with a 4096-token history, one query token, bf16 inputs with fp32
+accumulation, one layer's cache (8 MiB of K+V), seeded N(0,1) data in blocks
+scattered over a pool twice the size the history needs.
+
+A step is one decode call through the C ABI: the split-KV decode kernel with
+its in-launch split merge, on a plan and workspace prepared once (the plan
+stays valid while the lengths keep the same split layout). The timed region
+replays a HIP graph of K steps; each step reads a different copy of the
+pool, and the copies together exceed 1 GiB, so the 256 MiB Infinity Cache
+cannot serve the KV stream from one step to the next (cold HBM).
+
+Printed: one JSON line with KV GB/s (whole job), microseconds per step, the
+decode kernel's roofline against 8 TB/s HBM and the float64 oracle's
+throughput on this host's cores. Before any timing the GPU output is checked
+against the oracle (atol = rtol = 1e-2).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode KV GB/s (% HBM peak) and µs/step, Llama-3.2-1B shape @4K history"
+PEAK_HBM_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_llama_L4096_pmc.md")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_decode.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current decode kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    m = re.search(r"^traffic-json: (\{.*\})\s*$", open(PMC_SUMMARY).read(), re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_sha") != kernel_source_sha():
+        return None
+    return rec
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--history", type=int, default=4096)
+    ap.add_argument("--pool-bytes", type=float, default=float(1 << 30),
+                    help="total bytes of rotated pool copies (cold-cache measurement)")
+    ap.add_argument("--warm", action="store_true",
+                    help="one pool copy only (reported as MALL-warm, not the headline)")
+    ap.add_argument("--combine-mode", type=int, default=0)
+    ap.add_argument("--blocks-per-split", type=int, default=0)
+    ap.add_argument("--wgs-per-cu", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="short run for hardware counters: a few decode steps and a plain "
+                         "256 MiB copy, no timing")
+    return ap.parse_args(argv)
+
+
+def cpu_baseline(inp, seconds: float):
+    """Time the float64 oracle (gather, then dense softmax attention) on the
+    same workload; best-of, the inputs already converted to float64."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    q = inp.q.double().numpy()
+    k = inp.k_pool.double().numpy()
+    v = inp.v_pool.double().numpy()
+    bt = inp.block_table.numpy().astype(np.int64)
+    lens = inp.context_lens.numpy().astype(np.int64)
+    times = []
+    with threadpool_limits(limits=1):
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end or len(times) < 5:
+            t0 = time.perf_counter()
+            oracle.paged_attention(q, k, v, bt, lens, scale=inp.scale)
+            times.append(time.perf_counter() - t0)
+    best = min(times)
+    return {
+        "value": round(inp.kv_bytes() / best / 1e9, 4), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": (f"full workload (1 sequence, 32 heads, {int(inp.context_lens[0])} tokens), "
+                   f"float64 numpy, 1 BLAS thread, best of {len(times)} runs "
+                   f"(median {sorted(times)[len(times) // 2] * 1e3:.2f} ms) in "
+                   f"{sum(times):.1f} s"),
+        "ms_per_step": round(best * 1e3, 3),
+    }
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU leg "
+              "(decode shards by sequence or KV head with no exchange inside the path); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_178_amd import binding
+    from paged_kv_cache_178_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    inp = wl.llama_decode(args.history)
+    kv_bytes = inp.kv_bytes()
+    log(f"[bench] workload {inp.name}: {kv_bytes} KV bytes, pool {tuple(inp.k_pool.shape)}")
+
+    q = inp.q.to(dev)
+    bt = inp.block_table.to(dev)
+    lens = inp.context_lens.to(dev)
+    pool_bytes = 2 * inp.k_pool.numel() * inp.k_pool.element_size()
+    copies = 1 if args.warm else max(1, math.ceil(args.pool_bytes / pool_bytes))
+    kbig = inp.k_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+    vbig = inp.v_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+    out = torch.empty_like(q)
+    log(f"[bench] {copies} pool copies ({copies * pool_bytes / 2**20:.0f} MiB)")
+
+    opts = binding.PlanOpts(combine_mode=args.combine_mode,
+                            force_blocks_per_split=args.blocks_per_split,
+                            wgs_per_cu=args.wgs_per_cu, num_cus=props.multi_processor_count)
+    desc = binding.make_desc(q, kbig[0], bt, out=out, scale=inp.scale)
+    lens_h = inp.context_lens.numpy()
+    bt_h = inp.block_table.numpy()
+    st = binding.np_check_paged_inputs(desc, q, kbig[0], vbig[0], bt, lens, out, bt_h, lens_h)
+    if st:
+        raise binding.NPError(st, "np_check_paged_inputs")
+    plan = binding.np_plan(desc, lens_h, None, opts)
+    ws = binding.workspace_for(plan, dev)
+    grid, wg, comb = plan.launch_shape()
+    log(f"[bench] plan: blocks/split {plan.blocks_per_split}, splits {plan.max_splits}, "
+        f"grid {grid}, combine wgs {comb}, workspace {plan.workspace_bytes} B")
+
+    def graph_us(fn, n: int) -> float:
+        """Average device time per call of n calls captured in one HIP graph."""
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    def event_us(fn, n: int):
+        """Mean of per-call event intervals around n eager calls."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record()
+            fn(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        t = np.array([x.elapsed_time(y) * 1e3 for x, y in evs])
+        return float(t.mean()), t
+
+    def step(i: int) -> None:
+        c = i % copies
+        binding.np_paged_attention_decode(desc, plan, q, kbig[c], vbig[c], bt, lens, out, ws)
+
+    if args.pmc_probe:
+        for i in range(10):
+            step(i)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] pmc probe done: 10 decode steps, 3 copies of 268435456 bytes")
+        return 0
+
+    # ---- parity gate (on copy 0) before any timing
+    import oracle
+
+    step(0)
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                 inp.context_lens, scale=inp.scale)
+    got = out.to("cpu", torch.float64).numpy()
+    err = np.abs(got - ref)
+    if not (err <= 1e-2 + 1e-2 * np.abs(ref)).all():
+        print(f"bench.py: parity gate failed, max abs err {err.max():.3e}", file=sys.stderr)
+        return 1
+    log(f"[bench] parity gate passed: max abs err {err.max():.3e}")
+
+    # ---- warmup
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: one graph of K steps, each on its own pool copy
+    K = args.steps
+    us_per_step = graph_us(step, K)
+    log(f"[bench] graph: {K} steps -> {us_per_step:.3f} us/step")
+
+    # ---- the decode kernel alone: events around each eager launch
+    kernel_us, launch_us = event_us(step, K)
+    log(f"[bench] per-launch events: mean {kernel_us:.3f} us, median "
+        f"{float(np.median(launch_us)):.3f} us, min {float(launch_us.min()):.3f} us")
+
+    # ---- reference kernels: the empty-kernel floor and a plain read of the
+    # same number of bytes (cold, rotating over the same pool copies)
+    sink = torch.empty(grid[0] * 256, dtype=torch.int32, device=dev)
+    kflat = kbig.view(copies, -1)
+    read_bytes = kv_bytes // 2 * 2                      # == K half + V half
+    src_elems = read_bytes // kbig.element_size()
+
+    def probe_read(i):
+        binding.np_probe_stream_read(kflat[i % copies, :src_elems], grid[0], sink)
+
+    def probe_empty(i):
+        binding.np_probe_empty()
+
+    empty_us = graph_us(probe_empty, K)
+    read_us = graph_us(probe_read, K)
+    read_ev_us, _ = event_us(probe_read, K)
+    log(f"[bench] probes (graph): empty kernel {empty_us:.3f} us, stream read of {read_bytes} B "
+        f"{read_us:.3f} us ({read_bytes / read_us / 1e3:.1f} GB/s)")
+
+    # ---- eager steps with host validation and planning each step
+    t_host = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        th = time.perf_counter()
+        c = i % copies
+        st = binding.np_check_paged_inputs(desc, q, kbig[c], vbig[c], bt, lens, out,
+                                           None, lens_h)
+        p2 = binding.np_plan(desc, lens_h, None, opts)
+        t_host.append(time.perf_counter() - th)
+        binding.np_paged_attention_decode(desc, p2, q, kbig[c], vbig[c], bt, lens, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / K
+    host_us = float(np.median(t_host)) * 1e6
+    log(f"[bench] eager with per-step check+plan: {eager_us:.2f} us/step "
+        f"(host check+plan via ctypes {host_us:.2f} us)")
+
+    gbs = kv_bytes / (us_per_step * 1e-6) / 1e9
+    achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
+    traffic = stored_traffic()
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"paged decode, Llama-3.2-1B head shape, {args.history}-token history, "
+                        "1 layer, batch 1",
+            "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 64, "block_size": 16,
+            "batch": 1, "history": args.history, "kv_bytes_per_step": kv_bytes,
+            "accumulate": "fp32",
+            "cache": "MALL-warm (one pool)" if args.warm else
+                     f"cold: {copies} rotating pool copies, {copies * pool_bytes >> 20} MiB",
+            "blocks_per_split": plan.blocks_per_split, "splits": plan.max_splits,
+            "grid": list(grid), "combine": "separate kernel" if comb else "in-launch",
+        },
+        "us_per_step": round(us_per_step, 3),
+        "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": (None if traffic is None else traffic["traffic_bytes_per_launch"]),
+            "kernel": "paged_decode_kernel (bf16, d_pad 64, group 4, block 16, in-launch merge)",
+            "kernel_us_events": round(kernel_us, 3),
+        },
+        "eager_us_per_step_with_host_plan": round(eager_us, 3),
+        "host_check_plan_us": round(host_us, 3),
+        "probes": {
+            "empty_kernel_us_graph": round(empty_us, 3),
+            "stream_read_bytes": read_bytes,
+            "stream_read_us_graph": round(read_us, 3),
+            "stream_read_gbs_graph": round(read_bytes / read_us / 1e3, 2),
+            "stream_read_us_events": round(read_ev_us, 3),
+            "note": "same grid size as the decode, cold rotating copies",
+        },
+        "parity_max_abs_err": float(err.max()),
+        "device": props.name,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

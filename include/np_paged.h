@@ -95,10 +95,14 @@ typedef struct np_paged_desc {
 /* Planner knobs; pass NULL for the defaults. */
 typedef struct np_plan_opts {
   int32_t num_cus;                /* compute units to fill; 0 => 256           */
-  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 2          */
+  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 1          */
   int32_t min_blocks_per_split;   /* 0 => 4                                    */
   int32_t max_blocks_per_split;   /* 0 => 1024 tokens' worth of blocks         */
   int32_t force_blocks_per_split; /* > 0: use exactly this split size          */
+  int32_t combine_mode;           /* 0: the last split workgroup of each
+                                     (sequence, KV head) merges the splits in
+                                     the same launch; 1: a separate combine
+                                     kernel does it                            */
   int32_t reserved;               /* must be 0                                 */
 } np_plan_opts;
 
@@ -174,8 +178,12 @@ int32_t np_next_pow2(int32_t x);
  * sequence has more than one split, the combine kernel, asynchronously on
  * `stream` (a hipStream_t; NULL = the null stream). Never allocates, never
  * synchronises. `workspace` (device, 256-byte aligned) must hold
- * np_plan_workspace_bytes(plan) bytes; its contents need not be initialised
- * and are scratch after the call. Checks the descriptor and pointers (not
+ * np_plan_workspace_bytes(plan) bytes. Its first bytes hold one 32-bit
+ * arrival counter per (sequence, KV head): they must be zero before the first
+ * call that uses the workspace (allocate it zeroed) and every call leaves them
+ * zero again; the rest is scratch. Two calls that share a workspace must not
+ * overlap in time (same stream, or ordered by events). Checks the descriptor
+ * and pointers (not
  * the device arrays' values) and that the plan was made for this descriptor.
  * Built kernels: block_size 16; head_dim a multiple of 8 (16-bit types) or 4
  * (fp32) up to 128; Hq/Hkv from 1 to 8. Other valid shapes return
@@ -204,6 +212,18 @@ np_status np_paged_attention_prefill(const np_paged_desc* desc, const np_plan_t*
                                      const int32_t* context_lens, const int32_t* q_start,
                                      void* out, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/*
+ * Reference kernels for measurement (not part of the attention path).
+ * np_probe_empty launches one empty workgroup: the per-kernel floor.
+ * np_probe_stream_read reads `bytes` (a multiple of 16) from 16-byte-aligned
+ * device memory `src` once, with `num_wgs` workgroups of 256 threads, and
+ * writes one 32-bit word per thread to `sink` (device, at least num_wgs * 1024
+ * bytes). Both are asynchronous on `stream`.
+ */
+np_status np_probe_empty(void* stream);
+np_status np_probe_stream_read(const void* src, size_t bytes, uint32_t num_wgs, void* sink,
+                               size_t sink_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* np_status_string(np_status status);

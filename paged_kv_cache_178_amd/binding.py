@@ -49,7 +49,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [
         ("num_cus", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32),
         ("min_blocks_per_split", ctypes.c_int32), ("max_blocks_per_split", ctypes.c_int32),
-        ("force_blocks_per_split", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("force_blocks_per_split", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -97,6 +98,11 @@ def _lib():
         lib.np_paged_attention_prefill.restype = ctypes.c_int
         lib.np_paged_attention_prefill.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P,
                                                    _P, _P, _P, _P, ctypes.c_size_t, _P]
+        lib.np_probe_empty.restype = ctypes.c_int
+        lib.np_probe_empty.argtypes = [_P]
+        lib.np_probe_stream_read.restype = ctypes.c_int
+        lib.np_probe_stream_read.argtypes = [_P, ctypes.c_size_t, ctypes.c_uint32, _P,
+                                             ctypes.c_size_t, _P]
         _LIB = lib
     return _LIB
 
@@ -275,12 +281,14 @@ def np_paged_attention_prefill(desc: Desc, plan: Plan, q, k_pool, v_pool, block_
 
 
 def workspace_for(plan: Plan, device):
-    """A device byte buffer of the plan's workspace size (256-byte aligned by
-    the caching allocator), or None when the plan needs none."""
+    """A zeroed device byte buffer of the plan's workspace size (256-byte
+    aligned by the caching allocator), or None when the plan needs none. The
+    library leaves its arrival counters zero after every call, so the buffer
+    can be reused by later calls on the same stream."""
     import torch
 
     n = plan.workspace_bytes
-    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+    return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def decode(q, k_pool, v_pool, block_table, context_lens, out=None, scale=None,
@@ -321,6 +329,20 @@ def prefill(q, k_pool, v_pool, block_table, context_lens, q_start, out=None, sca
     np_paged_attention_prefill(desc, plan, q, k_pool, v_pool, block_table, context_lens,
                                q_start, out, ws)
     return out
+
+
+def np_probe_empty(stream=None) -> None:
+    st = _lib().np_probe_empty(_stream(stream))
+    if st:
+        raise NPError(st, "np_probe_empty")
+
+
+def np_probe_stream_read(src, num_wgs: int, sink, stream=None) -> None:
+    st = _lib().np_probe_stream_read(_ptr(src), src.numel() * src.element_size(), int(num_wgs),
+                                     _ptr(sink), sink.numel() * sink.element_size(),
+                                     _stream(stream))
+    if st:
+        raise NPError(st, "np_probe_stream_read")
 
 
 def default_scale(head_dim: int) -> float:

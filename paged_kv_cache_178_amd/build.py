@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnp_paged.so")
 
-HIP_SOURCES = ["np_decode.hip", "np_prefill.hip"]
+HIP_SOURCES = ["np_decode.hip", "np_prefill.hip", "np_probe.hip"]
 HOST_SOURCES = ["np_host.cpp"]
 
 HIPCC_FLAGS = [

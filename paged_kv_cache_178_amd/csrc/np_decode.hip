@@ -17,16 +17,16 @@
 // * A K or V row of one head (d_pad channels) is covered by LPR lanes with one
 //   16-byte load each (8 lanes x 16 B = 128 B for bf16/fp16 d=64, one cache
 //   line). One wave load therefore covers TPL = 64/LPR consecutive slots.
-// * Waves take whole blocks round-robin and prefetch the next block's K/V into
-//   registers while computing the current one.
-// * Each group of LPR lanes ("row") runs its own online softmax over the slots
-//   it sees ("What a Kernel Is ...", "Technical Details": running max and
-//   sum). No cross-lane max is needed in the loop; the only cross-lane work is
-//   the LPR-lane sum of the QK partial dot products (DPP).
-// * The running max is only moved when a score exceeds it by more than
-//   kLazy (log2 units), so the accumulator is rarely rescaled; weights stay
-//   below 2^kLazy, which fp32 holds exactly as well as weights below 1.
-// * At the end the rows and waves are merged through LDS.
+// * Waves take whole blocks round-robin and issue all K/V loads of a group of
+//   blocks before computing any of them.
+// * The lanes of a row each hold VEC channels of one slot; the only
+//   cross-lane work per block is the LPR-lane sum of the QK partial dot
+//   products (DPP). Weights and V of two slots are packed so P.V is a v_dot2.
+// * Scores of a group of blocks are computed first; the wave-wide max of the
+//   group moves the running max once, so earlier sums are rescaled once per
+//   group and the block bodies carry no branches.
+// * The online-softmax max is shared by a whole wave, so at the end the rows
+//   of a wave add directly and the waves are merged through LDS.
 // Scores are kept in log2 units (scale * log2 e folded in), exp2 is v_exp_f32.
 
 #include <hip/hip_runtime.h>
@@ -40,7 +40,6 @@ namespace np {
 
 namespace {
 
-constexpr float kLazy = 8.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
@@ -50,6 +49,7 @@ struct DecodeParams {
   const int32_t* bt;
   const int32_t* lens;
   void* out;
+  uint32_t* ws_cnt;
   float* ws_ml;
   float* ws_acc;
   int64_t q_s0, q_s1;
@@ -192,9 +192,186 @@ __device__ __forceinline__ uint4 load16(const void* base, int64_t elem_off, int 
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem_off * elt);
 }
 
+// Split partials are published with agent-scope relaxed atomic stores and
+// read back with agent-scope relaxed atomic loads. On gfx950 these are plain
+// 64-bit global stores/loads with the device-coherence bit set, so the partials
+// bypass the per-XCD L2 and no L2 write-back or invalidate (what an agent-scope
+// fence costs, per workgroup) is needed. The writer waits for its stores to
+// complete before it takes its arrival ticket; the reader issues its loads only
+// after seeing that every other ticket was taken.
+__device__ __forceinline__ void publish2(float* p, float a, float b) {
+  const uint64_t v = uint64_t(__float_as_uint(a)) | (uint64_t(__float_as_uint(b)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 fetch2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
+}
+
+// Merge the splits of one (sequence, KV head): with M = max_j m_j,
+// out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j. This is the split-KV
+// page's log-sum-exp combine written with unnormalised partials
+// (lse_j = m_j + log l_j, out_j = acc_j / l_j, in log2 units).
+//
+// Latency-parallel: waves take splits round-robin, each lane owns float4
+// chunks of the G x d_pad output, and a batch of UB splits has all its loads
+// in flight before any is used; the per-wave states are merged through LDS.
+template <int DT, int D_PAD, int G>
+__device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh,
+                                             int splits) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
+  constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
+  constexpr int UB = CPL > 1 ? 8 : 16;
+  const int wave = threadIdx.x / kWaveSize;
+  const int lane = threadIdx.x % kWaveSize;
+  const int64_t part_base = (int64_t(s) * p.hq + int64_t(kvh) * G) * p.max_splits;
+
+  float mw[CPL], dw[CPL];
+  float4 nw[CPL];
+#pragma unroll
+  for (int ci = 0; ci < CPL; ++ci) {
+    mw[ci] = -INFINITY;
+    dw[ci] = 0.0f;
+    nw[ci] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int j0 = wave; j0 < splits; j0 += NW * UB) {
+    float2 ml[UB][CPL];
+    float2 a0[UB][CPL], a1[UB][CPL];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int j = j0 + u * NW;
+#pragma unroll
+      for (int ci = 0; ci < CPL; ++ci) {
+        const int chunk = lane + ci * kWaveSize;
+        ml[u][ci] = make_float2(-INFINITY, 0.0f);
+        a0[u][ci] = make_float2(0.f, 0.f);
+        a1[u][ci] = make_float2(0.f, 0.f);
+        if (j < splits && chunk < NCH) {
+          const int h = (chunk * 4) / D_PAD;
+          const int c = (chunk * 4) % D_PAD;
+          const int64_t part = part_base + int64_t(h) * p.max_splits + j;
+          ml[u][ci] = fetch2(p.ws_ml + 2 * part);
+          a0[u][ci] = fetch2(p.ws_acc + part * D_PAD + c);
+          a1[u][ci] = fetch2(p.ws_acc + part * D_PAD + c + 2);
+        }
+      }
+    }
+#pragma unroll
+    for (int ci = 0; ci < CPL; ++ci) {
+      float mx = mw[ci];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) mx = fmaxf(mx, ml[u][ci].x);
+      if (mx == -INFINITY) continue;
+      const float a = __builtin_amdgcn_exp2f(mw[ci] - mx);
+      float d = dw[ci] * a;
+      float4 n = make_float4(nw[ci].x * a, nw[ci].y * a, nw[ci].z * a, nw[ci].w * a);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const float w = __builtin_amdgcn_exp2f(ml[u][ci].x - mx);
+        d = fmaf(w, ml[u][ci].y, d);
+        n.x = fmaf(w, a0[u][ci].x, n.x);
+        n.y = fmaf(w, a0[u][ci].y, n.y);
+        n.z = fmaf(w, a1[u][ci].x, n.z);
+        n.w = fmaf(w, a1[u][ci].y, n.w);
+      }
+      mw[ci] = mx;
+      dw[ci] = d;
+      nw[ci] = n;
+    }
+  }
+  __shared__ float s_m[NW][CPL * kWaveSize];
+  __shared__ float s_d[NW][CPL * kWaveSize];
+  __shared__ float4 s_n[NW][CPL * kWaveSize];
+#pragma unroll
+  for (int ci = 0; ci < CPL; ++ci) {
+    s_m[wave][lane + ci * kWaveSize] = mw[ci];
+    s_d[wave][lane + ci * kWaveSize] = dw[ci];
+    s_n[wave][lane + ci * kWaveSize] = nw[ci];
+  }
+  __syncthreads();
+  for (int chunk = threadIdx.x; chunk < NCH; chunk += blockDim.x) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w][chunk]);
+    float d = 0.0f;
+    float4 n = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = __builtin_amdgcn_exp2f(s_m[w][chunk] - mx);   // 0 for idle waves
+      d = fmaf(a, s_d[w][chunk], d);
+      n.x = fmaf(a, s_n[w][chunk].x, n.x);
+      n.y = fmaf(a, s_n[w][chunk].y, n.y);
+      n.z = fmaf(a, s_n[w][chunk].z, n.z);
+      n.w = fmaf(a, s_n[w][chunk].w, n.w);
+    }
+    const int h = (chunk * 4) / D_PAD;
+    const int c = (chunk * 4) % D_PAD;
+    const int64_t o = int64_t(s) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1 + c;
+    const float r = 1.0f / d;
+    if (c + 0 < p.head_dim) store_out<DT>(p.out, o + 0, n.x * r);
+    if (c + 1 < p.head_dim) store_out<DT>(p.out, o + 1, n.y * r);
+    if (c + 2 < p.head_dim) store_out<DT>(p.out, o + 2, n.z * r);
+    if (c + 3 < p.head_dim) store_out<DT>(p.out, o + 3, n.w * r);
+  }
+}
+
+// ------------------------------------------------------- math helpers
+
+// Max over the rows of a wave (lanes that differ in the row index); the LPR
+// lanes of one row already hold the same value. Result is wave-uniform.
+template <int LPR>
+__device__ __forceinline__ float wave_max_rows(float x) {
+  if constexpr (LPR <= 8) x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8 (lane i <-> i^8)
+  if constexpr (LPR <= 16)
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(
+                                               __builtin_bit_cast(int, x), 0x401F)));   // i^16
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  return fmaxf(lo, hi);
+}
+
+// P.V for one pair of slots (ja, jb) held by this lane, 16-bit types: the two
+// slots' V values of each channel are packed side by side (v_perm) and the
+// two weights are rounded to the input type, so one v_dot2 adds both slots'
+// contributions of a channel in fp32.
+template <int DT, int G, int VEC>
+__device__ __forceinline__ void pv_pair(const uint4& va, const uint4& vb, const float (*w)[G],
+                                        int ja, int jb, float (*acc)[VEC]) {
+  const uint32_t a[4] = {va.x, va.y, va.z, va.w};
+  const uint32_t b[4] = {vb.x, vb.y, vb.z, vb.w};
+  uint32_t pr[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pr[2 * k] = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);       // low halves
+    pr[2 * k + 1] = __builtin_amdgcn_perm(b[k], a[k], 0x07060302u);   // high halves
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    typedef __attribute__((ext_vector_type(2))) float f2_t;
+    const f2_t ww = {w[ja][h], w[jb][h]};
+    if constexpr (DT == NP_BF16) {
+      const bf16x2_t wp = __builtin_convertvector(ww, bf16x2_t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[h][c] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, pr[c]),
+                                                    acc[h][c], false);
+    } else {
+      const f16x2_t wp = __builtin_convertvector(ww, f16x2_t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[h][c] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), acc[h][c],
+                                           false);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ kernel
 
-template <int DT, int D_PAD, int G, int BS>
+template <int DT, int D_PAD, int G, int BS, bool FUSED>
 __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     const DecodeParams p) {
   constexpr int kElt = Elt<DT>::kBytes;
@@ -203,24 +380,41 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   constexpr int TPL = kWaveSize / LPR;    // slots per wave-load
   static_assert(LPR >= 1 && LPR <= 32 && BS % TPL == 0, "unsupported tile shape");
   constexpr int NLB = BS / TPL;           // wave-loads per block (per K or V)
+  static_assert(NLB % 2 == 0, "slots of a block are paired for P.V");
+  constexpr int NG = 4 / NLB > 1 ? 4 / NLB : 1;   // blocks per load group
   constexpr int NW = kDecodeWaves;
 
   const int kvh = blockIdx.x % p.hkv;
   const int split = blockIdx.x / p.hkv;
   const int s = blockIdx.y;
-  const int L = p.lens[s];
-  int nb = (L + BS - 1) / BS;
-  nb = nb < p.max_blocks ? nb : p.max_blocks;
-  const int splits = (nb + p.bps - 1) / p.bps;
-  if (split >= splits) return;
   const int b0 = split * p.bps;
-  const int b1 = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
-
-  const int wave = threadIdx.x / kWaveSize;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int lane = threadIdx.x % kWaveSize;
   const int row = lane / LPR;
   const int ch0 = (lane % LPR) * VEC;
   const bool chan_ok = ch0 < p.head_dim;
+  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+
+  // This wave's blocks are b0 + wave + i * NW. It takes them in groups of NG:
+  // all K/V loads of a group are issued before any of its blocks is used, and
+  // the table entries of the next group are read while this group computes.
+  // The first group's entries are read before the context length is known
+  // (table reads are clamped to the row, so they stay in bounds), which takes
+  // one dependent memory round trip off the start of the kernel.
+  int ph[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int b = b0 + wave + i * NW;
+    ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
+  }
+  const int L = p.lens[s];
+  int nb = (L + BS - 1) / BS;
+  nb = nb < p.max_blocks ? nb : p.max_blocks;
+  int splits = (nb + p.bps - 1) / p.bps;
+  splits = splits < p.max_splits ? splits : p.max_splits;
+  if (split >= splits) return;
+  const int b1 = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
+  const int nwb = (b1 - b0 - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
 
   // q chunks of the G heads of this group (zero in padded channels).
   uint4 qv[G];
@@ -231,6 +425,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
       qv[h] = load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + ch0, kElt);
   }
 
+  // Online-softmax state. m[h] is shared by the whole wave (wave-uniform);
+  // l[h] and acc[h][.] are this lane's partial sums over the slots it saw.
   float m[G], l[G], acc[G][VEC];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -240,141 +436,184 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     for (int e = 0; e < VEC; ++e) acc[h][e] = 0.0f;
   }
 
-  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
-  const int64_t head_off = int64_t(kvh) * p.kv_s2 + ch0;
+  // Loads are unconditional inside a valid block: slots past the history are
+  // still inside the block, and padded channels read the last real chunk
+  // instead; both are masked by selects below, never by multiplication.
+  const int ch_addr = chan_ok ? ch0 : p.head_dim - VEC;
+  const int64_t head_off = int64_t(kvh) * p.kv_s2 + ch_addr + int64_t(row) * p.kv_s1;
 
-  uint4 kc[NLB], vc[NLB];
-  auto issue = [&](int b, uint4* kk, uint4* vv) {
-    const int64_t base = int64_t(bt_row[b]) * p.kv_s0 + head_off;
+  for (int g0 = 0; g0 < nwb; g0 += NG) {
+    uint4 kr[NG][NLB], vr[NG][NLB];
 #pragma unroll
-    for (int j = 0; j < NLB; ++j) {
-      const int slot = j * TPL + row;
-      const bool ok = chan_ok && (b * BS + slot < L);
-      kk[j] = make_uint4(0, 0, 0, 0);
-      vv[j] = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        kk[j] = load16(p.k, base + int64_t(slot) * p.kv_s1, kElt);
-        vv[j] = load16(p.v, base + int64_t(slot) * p.kv_s1, kElt);
+    for (int i = 0; i < NG; ++i) {
+      if (g0 + i < nwb) {
+        const int64_t base = int64_t(ph[i]) * p.kv_s0 + head_off;
+#pragma unroll
+        for (int j = 0; j < NLB; ++j) {
+          kr[i][j] = load16(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
+          vr[i][j] = load16(p.v, base + int64_t(j * TPL) * p.kv_s1, kElt);
+        }
       }
     }
-  };
-
-  int b = b0 + wave;
-  if (b < b1) issue(b, kc, vc);
-  for (; b < b1; b += NW) {
-    uint4 kn[NLB], vn[NLB];
-    const bool more = b + NW < b1;
-    if (more) issue(b + NW, kn, vn);
-
-    // Scores of this row's NLB slots for the G heads (log2 units).
-    float sc[NLB][G];
+    if (g0 + NG < nwb) {
 #pragma unroll
-    for (int j = 0; j < NLB; ++j) {
-      const bool tok_ok = b * BS + j * TPL + row < L;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float dot = row_sum<LPR>(dot16<DT>(kc[j], qv[h], 0.0f));
-        sc[j][h] = tok_ok ? dot * p.scale_log2 : -INFINITY;
+      for (int i = 0; i < NG; ++i) {
+        const int b = b0 + wave + (g0 + NG + i) * NW;
+        ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
       }
     }
-    // Online softmax update, lazily moving the reference max.
+    // Pass 1: scores of every slot of the group (log2 units). Every block of
+    // the group is computed, so the group has a single path; a block past
+    // this wave's share gets a limit of 0, which masks all its slots (its
+    // loads were skipped and its registers are never used unmasked).
+    float sc[NG][NLB][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = sc[0][h];
-#pragma unroll
-      for (int j = 1; j < NLB; ++j) mx = fmaxf(mx, sc[j][h]);
-      if (mx > m[h] + kLazy) {
-        const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);   // 0 when m = -inf
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-        m[h] = mx;
-      }
-    }
-    float vf[NLB][VEC];
-#pragma unroll
-    for (int j = 0; j < NLB; ++j) unpack16<DT>(vc[j], vf[j]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      // m[h] is finite once the row has seen a valid slot; before that every
-      // sc is -inf and the row's weights must stay 0.
-      const float mref = m[h] == -INFINITY ? 0.0f : m[h];
+    for (int i = 0; i < NG; ++i) {
+      const int lim = g0 + i < nwb ? L : 0;
+      const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
 #pragma unroll
       for (int j = 0; j < NLB; ++j) {
-        const float w = __builtin_amdgcn_exp2f(sc[j][h] - mref);
-        l[h] += w;
+        const bool tok_ok = tok0 + j * TPL < lim;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(w, vf[j][e], acc[h][e]);
+        for (int h = 0; h < G; ++h) {
+          const float dot = row_sum<LPR>(dot16<DT>(kr[i][j], qv[h], 0.0f));
+          sc[i][j][h] = tok_ok ? dot * p.scale_log2 : -INFINITY;
+        }
       }
     }
-    if (more) {
+    // One online-softmax step per group: the wave-wide max of the group's
+    // scores becomes the new reference; earlier sums are rescaled once.
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = sc[0][0][h];
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int j = 0; j < NLB; ++j) mx = fmaxf(mx, sc[i][j][h]);
+      const float m_new = fmaxf(m[h], wave_max_rows<LPR>(mx));   // finite: block g0 is valid
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);   // 0 when m = -inf
+      m[h] = m_new;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
+    }
+    // Pass 2: weights and P.V.
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int lim = g0 + i < nwb ? L : 0;
+      const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
+      float w[NLB][G];
+#pragma unroll
+      for (int j = 0; j < NLB; ++j)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          w[j][h] = __builtin_amdgcn_exp2f(sc[i][j][h] - m[h]);   // 0 for masked slots
+          l[h] += w[j][h];
+        }
+      uint4 vv[NLB];
 #pragma unroll
       for (int j = 0; j < NLB; ++j) {
-        kc[j] = kn[j];
-        vc[j] = vn[j];
+        const bool tok_ok = tok0 + j * TPL < lim;
+        vv[j].x = tok_ok ? vr[i][j].x : 0u;
+        vv[j].y = tok_ok ? vr[i][j].y : 0u;
+        vv[j].z = tok_ok ? vr[i][j].z : 0u;
+        vv[j].w = tok_ok ? vr[i][j].w : 0u;
+      }
+      if constexpr (DT == NP_F32) {
+#pragma unroll
+        for (int j = 0; j < NLB; ++j) {
+          float vf[VEC];
+          unpack16<DT>(vv[j], vf);
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(w[j][h], vf[e], acc[h][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NLB; j += 2) pv_pair<DT, G, VEC>(vv[j], vv[j + 1], w, j, j + 1, acc);
       }
     }
   }
 
-  // ---- merge the NW x TPL row states of the workgroup through LDS.
+  // ---- merge: rows of a wave share m, so their sums add directly; waves are
+  // weighted by 2^(m_wave - M). One barrier.
   __shared__ float red_acc[NW][TPL][G][D_PAD];
-  __shared__ float red_m[NW * TPL * G];
-  __shared__ float red_l[NW * TPL * G];
-  __shared__ float red_w[NW * TPL * G];
-  __shared__ float fin_m[G];
-  __shared__ float fin_l[G];
+  __shared__ float red_l[NW][TPL][G];
+  __shared__ float red_m[NW][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) red_acc[wave][row][h][ch0 + e] = acc[h][e];
-    if (lane % LPR == 0) {
-      red_m[(wave * TPL + row) * G + h] = m[h];
-      red_l[(wave * TPL + row) * G + h] = l[h];
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float mm = -INFINITY;
-    for (int r = 0; r < NW * TPL; ++r) mm = fmaxf(mm, red_m[r * G + h]);
-    float ll = 0.0f;
-    for (int r = 0; r < NW * TPL; ++r) {
-      const float w = __builtin_amdgcn_exp2f(red_m[r * G + h] - mm);   // 0 for empty rows
-      red_w[r * G + h] = w;
-      ll += w * red_l[r * G + h];
-    }
-    fin_m[h] = mm;
-    fin_l[h] = ll;
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<float4*>(&red_acc[wave][row][h][ch0 + e]) =
+          make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+    if (lane % LPR == 0) red_l[wave][row][h] = l[h];
+    if (lane == 0) red_m[wave][h] = m[h];
   }
   __syncthreads();
 
+  // Two channels per thread.
   const bool direct = splits == 1;
-  for (int o = threadIdx.x; o < G * D_PAD; o += NW * kWaveSize) {
-    const int h = o / D_PAD;
-    const int c = o % D_PAD;
-    if (c >= p.head_dim) continue;
-    float tot = 0.0f;
+  for (int o = threadIdx.x; o < G * D_PAD / 2; o += NW * kWaveSize) {
+    const int h = o / (D_PAD / 2);
+    const int c = 2 * (o % (D_PAD / 2));
+    float mm = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < NW * TPL; ++r)
-      tot = fmaf(red_w[r * G + h], red_acc[r / TPL][r % TPL][h][c], tot);
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, red_m[w][h]);
+    float t0 = 0.0f, t1 = 0.0f, ll = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float ww = __builtin_amdgcn_exp2f(red_m[w][h] - mm);   // 0 for idle waves
+      float a0 = 0.0f, a1 = 0.0f, lw = 0.0f;
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        const float2 a = *reinterpret_cast<const float2*>(&red_acc[w][r][h][c]);
+        a0 += a.x;
+        a1 += a.y;
+        lw += red_l[w][r][h];
+      }
+      t0 = fmaf(ww, a0, t0);
+      t1 = fmaf(ww, a1, t1);
+      ll = fmaf(ww, lw, ll);
+    }
+    if (c >= p.head_dim) continue;
     const int hg = kvh * G + h;
     if (direct) {
-      store_out<DT>(p.out, int64_t(s) * p.o_s0 + int64_t(hg) * p.o_s1 + c, tot / fin_l[h]);
+      const float r = 1.0f / ll;
+      const int64_t oi = int64_t(s) * p.o_s0 + int64_t(hg) * p.o_s1 + c;
+      store_out<DT>(p.out, oi, t0 * r);
+      store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
     } else {
       const int64_t part = (int64_t(s) * p.hq + hg) * p.max_splits + split;
-      p.ws_acc[part * D_PAD + c] = tot;
-      if (c == 0) {
-        p.ws_ml[2 * part] = fin_m[h];
-        p.ws_ml[2 * part + 1] = fin_l[h];
-      }
+      publish2(p.ws_acc + part * D_PAD + c, t0, t1);
+      if (c == 0) publish2(p.ws_ml + 2 * part, mm, ll);
     }
+  }
+  if constexpr (FUSED) {
+    if (direct) return;
+    // Last-arriver merge: every thread waits until its partial stores are
+    // complete, then one thread takes a ticket; the workgroup holding the last
+    // ticket of its (sequence, KV head) merges all splits and resets the
+    // counter for the next call. Counters sit kCounterStride apart so tickets
+    // of different KV heads do not contend for one line.
+    __shared__ int last;
+    uint32_t* cnt = p.ws_cnt + int64_t(s * p.hkv + kvh) * kCounterStride;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == uint32_t(splits - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    merge_splits<DT, D_PAD, G>(p, s, kvh, splits);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Merge the splits of every (sequence, KV head) that was split: with
-// M = max_j m_j, out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j. This
-// is the split-KV page's log-sum-exp combine written with unnormalised
-// partials (lse_j = m_j + log l_j, out_j = acc_j / l_j).
+// Separate-launch merge of every (sequence, KV head) that was split.
 template <int DT, int D_PAD, int G, int BS>
 __global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams p) {
   const int kvh = blockIdx.x % p.hkv;
@@ -385,29 +624,17 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams p
   int splits = (nb + p.bps - 1) / p.bps;
   splits = splits < p.max_splits ? splits : p.max_splits;
   if (splits <= 1) return;
-  for (int o = threadIdx.x; o < G * D_PAD; o += blockDim.x) {
-    const int h = o / D_PAD;
-    const int c = o % D_PAD;
-    if (c >= p.head_dim) continue;
-    const int hg = kvh * G + h;
-    const int64_t part0 = (int64_t(s) * p.hq + hg) * p.max_splits;
-    float mm = -INFINITY;
-    for (int j = 0; j < splits; ++j) mm = fmaxf(mm, p.ws_ml[2 * (part0 + j)]);
-    float num = 0.0f, den = 0.0f;
-    for (int j = 0; j < splits; ++j) {
-      const float w = __builtin_amdgcn_exp2f(p.ws_ml[2 * (part0 + j)] - mm);
-      den = fmaf(w, p.ws_ml[2 * (part0 + j) + 1], den);
-      num = fmaf(w, p.ws_acc[(part0 + j) * D_PAD + c], num);
-    }
-    store_out<DT>(p.out, int64_t(s) * p.o_s0 + int64_t(hg) * p.o_s1 + c, num / den);
-  }
+  merge_splits<DT, D_PAD, G>(p, s, kvh, splits);
 }
 
 template <int DT, int D_PAD, int G>
 np_status launch_decode_t(const DecodeParams& prm, const np_plan_core& c, hipStream_t st) {
   constexpr int BS = 16;
   dim3 grid(c.grid[0], c.grid[1], c.grid[2]);
-  paged_decode_kernel<DT, D_PAD, G, BS><<<grid, dim3(c.wg_size), 0, st>>>(prm);
+  if (c.fused_combine)
+    paged_decode_kernel<DT, D_PAD, G, BS, true><<<grid, dim3(c.wg_size), 0, st>>>(prm);
+  else
+    paged_decode_kernel<DT, D_PAD, G, BS, false><<<grid, dim3(c.wg_size), 0, st>>>(prm);
   if (hipGetLastError() != hipSuccess) return NP_ERR_HIP;
   if (c.combine_wgs) {
     split_combine_kernel<DT, D_PAD, G, BS><<<dim3(c.combine_wgs), dim3(256), 0, st>>>(prm);
@@ -476,6 +703,9 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
   prm.bt = block_table;
   prm.lens = context_lens;
   prm.out = out;
+  prm.ws_cnt = c.ws_bytes
+                   ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + c.ws_cnt_off)
+                   : nullptr;
   prm.ws_ml = c.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + c.ws_ml_off)
                          : nullptr;
   prm.ws_acc = c.ws_bytes

@@ -168,10 +168,11 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
   np_plan_opts o{};
   if (opts) o = *opts;
   if (o.reserved != 0 || o.num_cus < 0 || o.wgs_per_cu < 0 || o.min_blocks_per_split < 0 ||
-      o.max_blocks_per_split < 0 || o.force_blocks_per_split < 0)
+      o.max_blocks_per_split < 0 || o.force_blocks_per_split < 0 || o.combine_mode < 0 ||
+      o.combine_mode > 1)
     return NP_ERR_BAD_SHAPE;
   const int32_t num_cus = o.num_cus ? o.num_cus : 256;
-  const int32_t wgs_per_cu = o.wgs_per_cu ? o.wgs_per_cu : 2;
+  const int32_t wgs_per_cu = o.wgs_per_cu ? o.wgs_per_cu : 1;
   const int32_t min_bps = o.min_blocks_per_split ? o.min_blocks_per_split : 4;
   const int32_t max_bps = o.max_blocks_per_split
                               ? o.max_blocks_per_split
@@ -234,17 +235,18 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
         plan->items.insert(plan->items.end(), item, item + 5);
       }
     }
-    c.combine_wgs = any_split ? static_cast<uint32_t>(c.num_seqs * c.hkv) : 0;
+    c.fused_combine = any_split && o.combine_mode == 0;
+    c.combine_wgs =
+        (any_split && !c.fused_combine) ? static_cast<uint32_t>(c.num_seqs * c.hkv) : 0;
     if (any_split) {
+      auto round = [](size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; };
       const size_t n_part = size_t(c.num_seqs) * c.hq * c.max_splits;
-      c.ws_ml_off = 0;
-      const size_t ml_bytes = (n_part * 2 * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-      c.ws_acc_off = ml_bytes;
-      const size_t acc_bytes =
-          (n_part * c.d_pad * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-      c.ws_bytes = ml_bytes + acc_bytes;
+      c.ws_cnt_off = 0;
+      c.ws_ml_off = round(size_t(c.num_seqs) * c.hkv * kCounterStride * sizeof(uint32_t));
+      c.ws_acc_off = c.ws_ml_off + round(n_part * 2 * sizeof(float));
+      c.ws_bytes = c.ws_acc_off + round(n_part * c.d_pad * sizeof(float));
     } else {
-      c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
+      c.ws_cnt_off = c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
     }
   } else {
     // Chunked prefill: one workgroup per (sequence, KV head, tile). A tile is
@@ -266,7 +268,8 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     c.grid[2] = 1;
     c.wg_size = kPrefillWaves * kWaveSize;
     c.combine_wgs = 0;
-    c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
+    c.fused_combine = 0;
+    c.ws_cnt_off = c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
     for (int32_t s = 0; s < c.num_seqs; ++s) {
       const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
       for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {

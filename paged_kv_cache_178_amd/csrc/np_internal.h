@@ -17,6 +17,7 @@ constexpr int kPrefillWaves = 4;               // waves per prefill workgroup
 constexpr int kPrefillRowsPerWave = 32;        // query rows of one head per wave
 constexpr int kMaxGroup = 8;                   // largest Hq/Hkv with a kernel
 constexpr size_t kWsAlign = 256;
+constexpr int kCounterStride = 64;             // uint32 words between arrival counters
 
 // Sizes every launch depends on, fixed when the plan is made.
 struct np_plan_core {
@@ -32,8 +33,10 @@ struct np_plan_core {
   // launch
   uint32_t grid[3];
   uint32_t wg_size;
-  uint32_t combine_wgs;
+  uint32_t combine_wgs;     // workgroups of the separate combine kernel (0: none)
+  int32_t fused_combine;    // splits merged by the last arriving workgroup
   // workspace (bytes from the workspace base)
+  size_t ws_cnt_off;       // uint32 arrival counters [num_seqs][Hkv], kCounterStride apart
   size_t ws_ml_off;        // float2 (m, l) [num_seqs][Hq][max_splits]
   size_t ws_acc_off;       // float [num_seqs][Hq][max_splits][d_pad]
   size_t ws_bytes;

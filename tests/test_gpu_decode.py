@@ -44,14 +44,37 @@ def batching():
     return wl.continuous_batching()
 
 
-def test_continuous_batching(batching):
-    _run_parity(batching)
+@pytest.mark.parametrize("combine_mode", [0, 1])
+def test_continuous_batching(batching, combine_mode):
+    _run_parity(batching, binding.PlanOpts(combine_mode=combine_mode))
 
 
+def test_workspace_reuse_keeps_counters_zero():
+    """The same workspace serves repeated calls: the arrival counters are left
+    at zero by every call and the outputs repeat bit for bit."""
+    inp = wl.custom(40, [4096, 3000, 100], hq=32, hkv=8, d=64, dtype="bf16")
+    dev = H.to_device(inp)
+    desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], scale=inp.scale)
+    plan = binding.np_plan(desc, inp.context_lens)
+    ws = binding.workspace_for(plan, "cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(dev["q"])
+        binding.np_paged_attention_decode(desc, plan, dev["q"], dev["k_pool"], dev["v_pool"],
+                                          dev["block_table"], dev["context_lens"], out, ws)
+        torch.cuda.synchronize()
+        n_cnt = inp.num_seqs * inp.num_kv_heads
+        assert int(ws[: 256 * n_cnt].view(torch.int32).abs().sum()) == 0
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    H.assert_close(outs[0], H.oracle_out(inp), "bf16", "reuse")
+
+
+@pytest.mark.parametrize("combine_mode", [0, 1])
 @pytest.mark.parametrize("bps", [1, 2, 3, 4, 7, 8, 16, 64, 256])
-def test_split_count_invariance(bps):
+def test_split_count_invariance(bps, combine_mode):
     inp = wl.llama_decode(4096)
-    opts = binding.PlanOpts(force_blocks_per_split=bps)
+    opts = binding.PlanOpts(force_blocks_per_split=bps, combine_mode=combine_mode)
     _, got = _run_parity(inp, opts)
     base = H.gpu_decode(inp, opts=binding.PlanOpts(force_blocks_per_split=256))
     # Only fp32 rounding in the split merge differs; outputs are bf16.

@@ -134,7 +134,7 @@ def test_check_errors():
 # ----------------------------------------------------------------- planner
 
 
-def model_decode_plan(lens, bs, hkv, num_cus=256, wgs_per_cu=2, min_bps=4, max_bps=None,
+def model_decode_plan(lens, bs, hkv, num_cus=256, wgs_per_cu=1, min_bps=4, max_bps=None,
                       force=0):
     """Brute-force statement of the decode plan rule."""
     max_bps = max_bps or max(1, 1024 // bs)
@@ -198,7 +198,7 @@ def test_decode_plan_matches_model(seed):
     assert plan.work_items() == items
     grid, wg, comb = plan.launch_shape()
     assert grid == (max_splits * hkv, num_seqs, 1) and wg == 256
-    assert comb == (num_seqs * hkv if max_splits > 1 else 0)
+    assert comb == 0                        # default: splits merged in the same launch
     # Coverage: every (seq, kv head, block) exactly once; no empty item.
     seen = {}
     for s, kvh, split, b0, b1 in items:
@@ -212,9 +212,18 @@ def test_decode_plan_matches_model(seed):
     if max_splits > 1:
         n_part = num_seqs * hkv * 4 * max_splits
         r = lambda x: (x + 255) // 256 * 256
-        assert plan.workspace_bytes == r(n_part * 8) + r(n_part * 64 * 4)
+        assert plan.workspace_bytes == r(num_seqs * hkv * 256) + r(n_part * 8) + r(n_part * 64 * 4)
     else:
         assert plan.workspace_bytes == 0
+
+
+def test_separate_combine_mode():
+    lens = np.array([4096, 100], np.int32)
+    d = desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=600)
+    p = B.np_plan(d, lens, None, B.PlanOpts(combine_mode=1))
+    assert p.launch_shape()[2] == 16
+    with pytest.raises(B.NPError, match="BAD_SHAPE"):
+        B.np_plan(d, lens, None, B.PlanOpts(combine_mode=2))
 
 
 def test_decode_plan_deterministic():
@@ -226,10 +235,10 @@ def test_decode_plan_deterministic():
 
 
 def test_decode_plan_named_workloads():
-    # Llama-3.2-1B shape at 4096 tokens: 256 blocks x 8 KV heads over 512 WGs.
+    # Llama-3.2-1B shape at 4096 tokens: 256 blocks x 8 KV heads over 256 WGs.
     d = desc(num_seqs=1, hq=32, hkv=8, max_blocks=256, n_blocks=512)
     p = B.np_plan(d, np.array([4096], np.int32))
-    assert p.blocks_per_split == 4 and p.max_splits == 64
+    assert p.blocks_per_split == 8 and p.max_splits == 32
     # Continuous batching: sequences up to 1024 tokens stay unsplit.
     rng = np.random.default_rng(4)
     lens = rng.integers(128, 8192, size=64, endpoint=True).astype(np.int32)
