@@ -1,0 +1,117 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+stats: kernel-trace statistics (calls, average/min/max duration per kernel).
+pmc:   HBM traffic per launch of one kernel from two counter runs
+       (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by what the
+       same counter reads for a plain copy of known size in the same run.
+
+Usage:
+  python -m paged_kv_cache_178_amd.rocprof_summary stats STATS_CSV --out FILE --cmd "..."
+  python -m paged_kv_cache_178_amd.rocprof_summary pmc --fetch CSV --write CSV \
+      --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes N --kv-bytes N --sha SHA \
+      --out FILE --cmd "..."
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import statistics
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats(args) -> None:
+    rows = _rows(args.csv)
+    lines = [f"# Kernel trace: {args.title}", "", "Command:", "", "```", args.cmd, "```", "",
+             "| kernel | calls | average (ns) | min (ns) | max (ns) |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path, counter, substr):
+    vals = []
+    for r in _rows(path):
+        if r.get("Counter_Name") != counter:
+            continue
+        if substr in r.get("Kernel_Name", ""):
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def pmc(args) -> None:
+    fk = _per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+    wk = _per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    # The copy kernel also serves small set-up copies: keep its n_copies
+    # largest dispatches, which are the copies of known size.
+    fc = sorted(_per_dispatch(args.fetch, "FETCH_SIZE", args.copy_kernel))[-args.n_copies:]
+    wc = sorted(_per_dispatch(args.write, "WRITE_SIZE", args.copy_kernel))[-args.n_copies:]
+    if not (fk and wk and fc and wc):
+        raise SystemExit("missing dispatches for the kernel or the copy in the counter files")
+    # The copy reads and writes copy_bytes each: counter KiB -> bytes factors.
+    f_scale = args.copy_bytes / statistics.median(fc)
+    w_scale = args.copy_bytes / statistics.median(wc)
+    fetch_b = statistics.median(fk) * f_scale
+    write_b = statistics.median(wk) * w_scale
+    rec = {
+        "kernel_sha": args.sha,
+        "fetch_kib_per_dispatch": statistics.median(fk),
+        "write_kib_per_dispatch": statistics.median(wk),
+        "copy_fetch_kib": statistics.median(fc),
+        "copy_write_kib": statistics.median(wc),
+        "fetch_bytes_per_kib": f_scale,
+        "write_bytes_per_kib": w_scale,
+        "traffic_bytes_per_launch": round(fetch_b + write_b),
+        "kv_bytes_per_launch": args.kv_bytes,
+    }
+    lines = [
+        f"# HBM traffic: {args.title}", "",
+        "Commands (one counter per run):", "", "```", args.cmd, "```", "",
+        f"- decode kernel dispatches: {len(fk)} (FETCH_SIZE), {len(wk)} (WRITE_SIZE)",
+        f"- FETCH_SIZE median {rec['fetch_kib_per_dispatch']:.1f} KiB, WRITE_SIZE median "
+        f"{rec['write_kib_per_dispatch']:.1f} KiB per dispatch",
+        f"- plain copy of {args.copy_bytes} bytes: FETCH_SIZE {rec['copy_fetch_kib']:.1f} KiB, "
+        f"WRITE_SIZE {rec['copy_write_kib']:.1f} KiB -> {f_scale:.2f} and {w_scale:.2f} bytes "
+        "per counted KiB",
+        f"- scaled: {fetch_b:.0f} bytes fetched + {write_b:.0f} bytes written = "
+        f"{rec['traffic_bytes_per_launch']} bytes per launch; algorithmic K+V bytes "
+        f"{args.kv_bytes} (ratio {rec['traffic_bytes_per_launch'] / args.kv_bytes:.3f})",
+        "", f"traffic-json: {json.dumps(rec)}", ""]
+    open(args.out, "w").write("\n".join(lines))
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--out", required=True)
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--title", default="")
+    b = sub.add_parser("pmc")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--copy-kernel", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--n-copies", type=int, default=3)
+    b.add_argument("--kv-bytes", type=int, required=True)
+    b.add_argument("--sha", required=True)
+    b.add_argument("--out", required=True)
+    b.add_argument("--cmd", required=True)
+    b.add_argument("--title", default="")
+    args = ap.parse_args(argv)
+    (stats if args.mode == "stats" else pmc)(args)
+
+
+if __name__ == "__main__":
+    main()
