@@ -1,7 +1,300 @@
-// Chunked prefill over a paged cache (placeholder until the MFMA kernel lands).
+// Chunked prefill over a paged KV cache on the gfx950 matrix cores.
+//
+// What is computed ("I Wrote the Three Attention Kernels That Run LLM
+// Inference -- in Portable Triton, on a Free Colab T4", sections "What is
+// attention, really?", "1. Fused prefill attention" and "3. Paged KV-cache
+// attention"; "Day 23: the real triton.jit paged-attention kernel", section
+// "What I added today", for past): for query row i of sequence s (absolute
+// position past_s + i) and query head h,
+//   out[q_start[s]+i, h, :] = sum_{t <= past_s+i} softmax_t(scale <q, K_s[t]>) V_s[t]
+// with K_s[t], V_s[t] read through the block table, KV head h / G.
+//
+// Decomposition:
+// * One 256-thread workgroup (4 wave64) per (sequence, KV head, tile). A tile
+//   is 4 units; a unit is one query head of the GQA group times 32 query rows
+//   (units numbered head-fastest), so the waves of a workgroup share every
+//   K/V tile they stage: for G = 4 the four heads of the group.
+// * Key tiles of 64 keys (4 blocks of 16) are staged in LDS, double buffered:
+//   K as [key][channel] rows, V transposed to [channel][key]. Wave w loads
+//   block w of the tile (one table entry per wave).
+// * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = the wave's
+//   32 query rows held in registers), so each lane holds one query's scores:
+//   the online-softmax max and sum ("1. Fused prefill attention": stream K/V,
+//   reduce online, never materialise N x N) stay in the lane, plus one
+//   exchange with the lane 32 away.
+// * O^T += V^T P^T on the same MFMA: P^T stays in the registers it was
+//   computed in (rounded to the input type); the keys of each k-step are taken
+//   in the order those registers hold them and V^T is read from LDS in the
+//   same order.
+// * Scores are in log2 units (scale * log2 e folded in); exp2 is v_exp_f32.
+
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+#include <cstdint>
+
 #include "np_internal.h"
+
+namespace np {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kKT = 64;             // keys per staged tile
+constexpr int kD = 64;              // head_dim handled by this kernel
+constexpr int kKRow = kD + 8;       // K row pitch in LDS (elements): 144 bytes
+constexpr int kVRow = kKT + 4;      // V^T row pitch in LDS (elements): 136 bytes
+constexpr int kRows = kPrefillRowsPerWave;   // 32 query rows per unit
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* bt;
+  const int32_t* lens;
+  const int32_t* q_start;
+  void* out;
+  int64_t q_s0, q_s1;
+  int64_t kv_s0, kv_s1, kv_s2;
+  int64_t o_s0, o_s1;
+  int64_t bt_stride;
+  int32_t hkv, hq, group, max_blocks;
+  float scale_log2;
+};
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+template <int DT>
+__device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
+  if constexpr (DT == NP_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Two fp32 values rounded to the input type and packed (low = first).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2_t x = {a, b};
+  if constexpr (DT == NP_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+}
+
+__device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off) {
+  return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+}
+
+template <int DT, int BS>
+__global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kernel(
+    const PrefillParams p) {
+  static_assert(BS == 16, "a wave stages one 16-slot block per key tile");
+  constexpr int NW = kPrefillWaves;
+  static_assert(NW * BS == kKT, "one block per wave per key tile");
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kD * kVRow];
+
+  const int kvh = blockIdx.x % p.hkv;
+  const int tile = blockIdx.x / p.hkv;
+  const int s = blockIdx.y;
+  const int G = p.group;
+  const int row0 = p.q_start[s];
+  const int n_q = p.q_start[s + 1] - row0;
+  const int L = p.lens[s];
+  const int past = L - n_q;
+  const int nqb = (n_q + kRows - 1) / kRows;
+  const int units = G * nqb;
+  if (tile * NW >= units) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int lane = threadIdx.x % kWaveSize;
+  const int half = lane / 32;          // which 8 of a 16-wide k-step this lane feeds
+  const int col = lane % 32;           // this lane's query row within the unit
+
+  // This wave's unit (head, 32-row query block); idle waves still stage K/V.
+  const int unit = tile * NW + wave;
+  const bool active = unit < units;
+  const int h = active ? unit % G : 0;
+  const int q0 = active ? (unit / G) * kRows : 0;
+  // Last key any row of this wave sees, and of the whole workgroup.
+  const int q_last = (q0 + kRows < n_q ? q0 + kRows : n_q) - 1;
+  const int wave_last_key = active ? past + q_last : -1;
+  int wg_last_unit = tile * NW + NW - 1;
+  wg_last_unit = wg_last_unit < units ? wg_last_unit : units - 1;
+  const int wg_q_last_blk = wg_last_unit / G;
+  const int wg_q_last = ((wg_q_last_blk + 1) * kRows < n_q ? (wg_q_last_blk + 1) * kRows : n_q) - 1;
+  const int n_tiles = (past + wg_q_last) / kKT + 1;
+  const int wave_tiles = active ? wave_last_key / kKT + 1 : 0;
+
+  // Query rows of this lane in the four 16-channel k-chunks (B operand of S^T).
+  const int my_q = q0 + col;
+  const bool q_ok = active && my_q < n_q;
+  uint4 qreg[kD / 16];
+  {
+    const int64_t qoff = int64_t(row0 + (q_ok ? my_q : 0)) * p.q_s0 +
+                         int64_t(kvh * G + h) * p.q_s1 + 8 * half;
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c)
+      qreg[c] = q_ok ? ld16(p.q, qoff + 16 * c) : make_uint4(0, 0, 0, 0);
+  }
+
+  // Staging map: wave w stages block w of the key tile; lane (kp, cc) holds
+  // slots 2kp, 2kp+1 of that block, channels 8cc .. 8cc+7.
+  const int kp = lane / 8;
+  const int cc = lane % 8;
+  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+  int nb = (L + BS - 1) / BS;
+  nb = nb < p.max_blocks ? nb : p.max_blocks;
+  uint4 kst[2], vst[2];
+  auto stage_load = [&](int kt) {
+    const int blk = kt * NW + wave;
+    if (blk < nb) {
+      const int64_t base = int64_t(bt_row[blk]) * p.kv_s0 + int64_t(kvh) * p.kv_s2 + 8 * cc +
+                           int64_t(2 * kp) * p.kv_s1;
+      kst[0] = ld16(p.k, base);
+      kst[1] = ld16(p.k, base + p.kv_s1);
+      vst[0] = ld16(p.v, base);
+      vst[1] = ld16(p.v, base + p.kv_s1);
+    }
+  };
+  auto stage_store = [&](int kt, int buf) {
+    const int blk = kt * NW + wave;
+    const int key0 = wave * BS + 2 * kp;            // key index within the tile
+    const int t0 = kt * kKT + key0;                 // absolute key of slot 2kp
+    // V rows of keys past the history are zero (their weight is 0 and 0 * V
+    // must not turn into NaN); K rows there are masked by score selects.
+    const bool ok0 = blk < nb && t0 < L;
+    const bool ok1 = blk < nb && t0 + 1 < L;
+    *reinterpret_cast<uint4*>(&k_lds[buf][key0 * kKRow + 8 * cc]) = kst[0];
+    *reinterpret_cast<uint4*>(&k_lds[buf][(key0 + 1) * kKRow + 8 * cc]) = kst[1];
+    const uint32_t a[4] = {ok0 ? vst[0].x : 0u, ok0 ? vst[0].y : 0u, ok0 ? vst[0].z : 0u,
+                           ok0 ? vst[0].w : 0u};
+    const uint32_t b[4] = {ok1 ? vst[1].x : 0u, ok1 ? vst[1].y : 0u, ok1 ? vst[1].z : 0u,
+                           ok1 ? vst[1].w : 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // channel 8cc + 2j: low halves; channel 8cc + 2j + 1: high halves.
+      *reinterpret_cast<uint32_t*>(&vt_lds[buf][(8 * cc + 2 * j) * kVRow + key0]) =
+          __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&vt_lds[buf][(8 * cc + 2 * j + 1) * kVRow + key0]) =
+          __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+    }
+  };
+
+  float m = -INFINITY;   // running max of this lane's query (log2 units)
+  float l = 0.0f;        // this lane's half of the running sum
+  f32x16_t acc[kD / 32];
+#pragma unroll
+  for (int cb = 0; cb < kD / 32; ++cb) acc[cb] = f32x16_t{};
+
+  stage_load(0);
+  stage_store(0, 0);
+  if (n_tiles > 1) stage_load(1);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt < wave_tiles) {
+      const uint16_t* kl = k_lds[buf];
+      const uint16_t* vl = vt_lds[buf];
+      // S^T for the two 32-key halves of the tile.
+      f32x16_t st[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        st[b] = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < kD / 16; ++c) {
+          const uint4 a =
+              *reinterpret_cast<const uint4*>(&kl[(32 * b + col) * kKRow + 16 * c + 8 * half]);
+          st[b] = mfma<DT>(a, qreg[c], st[b]);
+        }
+      }
+      // Scale, mask (keys past this query's position or past the history),
+      // and the online-softmax step for this lane's query.
+      const int key_base = kt * kKT;
+      const bool need_mask = key_base + kKT - 1 > past + q0 || key_base + kKT > L;
+      const int q_pos = past + my_q;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = st[b][i] * p.scale_log2;
+          if (need_mask) {
+            const int key = key_base + 32 * b + 8 * (i / 4) + 4 * half + (i % 4);
+            x = (key <= q_pos && key < L) ? x : -INFINITY;
+          }
+          st[b][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);            // finite: key 0 is visible to every row
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+      // P^T in the input type, packed for the B operand: k-step ks uses the
+      // registers 8(ks%2) .. 8(ks%2)+7 of half ks/2.
+      uint4 pb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = __builtin_amdgcn_exp2f(st[ks / 2][8 * (ks % 2) + j] - m);
+          l += e[j];
+        }
+        pb[ks] = make_uint4(pack2<DT>(e[0], e[1]), pack2<DT>(e[2], e[3]),
+                            pack2<DT>(e[4], e[5]), pack2<DT>(e[6], e[7]));
+      }
+      // O^T += V^T P^T. Register j of k-step ks holds key
+      // 16 ks + 8 (j / 4) + 4 half + j % 4 of the tile; V^T is read in that order.
+#pragma unroll
+      for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint16_t* vrow = &vl[(32 * cb + col) * kVRow + 16 * ks + 4 * half];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+          acc[cb] = mfma<DT>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], acc[cb]);
+        }
+    }
+    if (kt + 1 < n_tiles) {
+      stage_store(kt + 1, buf ^ 1);
+      if (kt + 2 < n_tiles) stage_load(kt + 2);
+    }
+    __syncthreads();
+  }
+
+  if (!q_ok) return;
+  const float l_tot = l + __shfl_xor(l, 32);
+  const float r = 1.0f / l_tot;
+  const int64_t obase = int64_t(row0 + my_q) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1;
+#pragma unroll
+  for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = 32 * cb + 8 * g + 4 * half;
+      const uint2 v = make_uint2(pack2<DT>(acc[cb][4 * g] * r, acc[cb][4 * g + 1] * r),
+                                 pack2<DT>(acc[cb][4 * g + 2] * r, acc[cb][4 * g + 3] * r));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + ch) = v;
+    }
+}
+
+}  // namespace
+
+}  // namespace np
 
 using namespace np;
 
@@ -13,13 +306,47 @@ extern "C" np_status np_paged_attention_prefill(const np_paged_desc* desc,
                                                 const int32_t* q_start, void* out,
                                                 void* workspace, size_t workspace_bytes,
                                                 void* stream) {
-  (void)workspace; (void)workspace_bytes; (void)stream;
+  (void)workspace;
+  (void)workspace_bytes;
   np_status st = check_desc(desc);
   if (st != NP_OK) return st;
   st = check_pointers(desc, q, k_pool, v_pool, block_table, context_lens, out);
   if (st != NP_OK) return st;
   if (q_start == nullptr) return NP_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(q_start) % 4 != 0) return NP_ERR_MISALIGNED;
   st = check_plan(desc, plan, 1);
   if (st != NP_OK) return st;
-  return NP_ERR_UNSUPPORTED;
+  const np_plan_core& c = plan->core;
+  if ((c.dtype != NP_BF16 && c.dtype != NP_F16) || c.head_dim != kD || c.block_size != 16 ||
+      c.group > kMaxGroup)
+    return NP_ERR_UNSUPPORTED;
+  PrefillParams prm{};
+  prm.q = q;
+  prm.k = k_pool;
+  prm.v = v_pool;
+  prm.bt = block_table;
+  prm.lens = context_lens;
+  prm.q_start = q_start;
+  prm.out = out;
+  prm.q_s0 = desc->q_stride[0];
+  prm.q_s1 = desc->q_stride[1];
+  prm.kv_s0 = desc->kv_stride[0];
+  prm.kv_s1 = desc->kv_stride[1];
+  prm.kv_s2 = desc->kv_stride[2];
+  prm.o_s0 = desc->out_stride[0];
+  prm.o_s1 = desc->out_stride[1];
+  prm.bt_stride = desc->bt_stride;
+  prm.hkv = c.hkv;
+  prm.hq = c.hq;
+  prm.group = c.group;
+  prm.max_blocks = c.max_blocks;
+  const float scale = desc->scale > 0.0f ? desc->scale : 1.0f / std::sqrt(float(c.head_dim));
+  prm.scale_log2 = scale * kLog2e;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  dim3 grid(c.grid[0], c.grid[1], c.grid[2]);
+  if (c.dtype == NP_BF16)
+    paged_prefill_kernel<NP_BF16, 16><<<grid, dim3(c.wg_size), 0, hs>>>(prm);
+  else
+    paged_prefill_kernel<NP_F16, 16><<<grid, dim3(c.wg_size), 0, hs>>>(prm);
+  return hipGetLastError() == hipSuccess ? NP_OK : NP_ERR_HIP;
 }

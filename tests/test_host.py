@@ -343,6 +343,13 @@ def test_prefill_entry_errors_before_launch():
     st = lib.np_paged_attention_prefill(ctypes.byref(d), plan.handle, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, None, FAKE, None, 0, None)
     assert st == S["NP_ERR_NULL_PTR"]
+    for bad in (desc(num_seqs=2, hq=32, hkv=8, d=128, max_blocks=256, n_blocks=600, n_q_total=96),
+                desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=600, n_q_total=96,
+                     dtype=B.NP_F32)):
+        pb = B.np_plan(bad, lens, q_start)
+        st = lib.np_paged_attention_prefill(ctypes.byref(bad), pb.handle, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, None, 0, None)
+        assert st == S["NP_ERR_UNSUPPORTED"]
     dec = B.np_plan(desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=600), lens)
     st = lib.np_paged_attention_prefill(ctypes.byref(d), dec.handle, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, FAKE, FAKE, None, 0, None)
