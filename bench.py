@@ -17,6 +17,13 @@ Printed: one JSON line with KV GB/s (whole job), microseconds per step, the
 decode kernel's roofline against 8 TB/s HBM and the float64 oracle's
 throughput on this host's cores. Before any timing the GPU output is checked
 against the oracle (atol = rtol = 1e-2).
+
+Other workloads (not the headline, one JSON line each):
+  --workload batching  64 sequences, lengths uniform on [128, 8192], Llama head
+                       shape, 40000-block pool; KV GB/s against 8 TB/s.
+  --workload prefill   4 sequences x (2048 cached + 512 new rows), causal, Llama
+                       head shape; TFLOP/s of the exact causal FLOP count
+                       against the 2.5 PFLOP/s dense bf16 MFMA peak.
 """
 
 from __future__ import annotations
@@ -36,6 +43,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged-decode KV GB/s (% HBM peak) and µs/step, Llama-3.2-1B shape @4K history"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_llama_L4096_pmc.md")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_decode.hip")
 
@@ -68,6 +76,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=("decode", "batching", "prefill"), default="decode")
     ap.add_argument("--history", type=int, default=4096)
     ap.add_argument("--pool-bytes", type=float, default=float(1 << 30),
                     help="total bytes of rotated pool copies (cold-cache measurement)")
@@ -84,9 +93,10 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def cpu_baseline(inp, seconds: float):
+def cpu_baseline(inp, seconds: float, seqs=None, prefill=False):
     """Time the float64 oracle (gather, then dense softmax attention) on the
-    same workload; best-of, the inputs already converted to float64."""
+    same workload, or on the sequences `seqs` of it; best-of, the inputs
+    already converted to float64. Returns seconds per call and a description."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -97,23 +107,77 @@ def cpu_baseline(inp, seconds: float):
     v = inp.v_pool.double().numpy()
     bt = inp.block_table.numpy().astype(np.int64)
     lens = inp.context_lens.numpy().astype(np.int64)
+    qs = inp.q_start.numpy().astype(np.int64)
+    if seqs is not None:
+        rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+        n_q = np.array([qs[s + 1] - qs[s] for s in seqs])
+        q = q[rows]
+        bt = bt[list(seqs)]
+        lens = lens[list(seqs)]
+        qs = np.concatenate([[0], np.cumsum(n_q)])
     times = []
     with threadpool_limits(limits=1):
         t_end = time.perf_counter() + seconds
-        while time.perf_counter() < t_end or len(times) < 5:
+        while time.perf_counter() < t_end or len(times) < 3:
             t0 = time.perf_counter()
-            oracle.paged_attention(q, k, v, bt, lens, scale=inp.scale)
+            oracle.paged_attention(q, k, v, bt, lens, q_start=qs if prefill else None,
+                                   scale=inp.scale)
             times.append(time.perf_counter() - t0)
     best = min(times)
-    return {
-        "value": round(inp.kv_bytes() / best / 1e9, 4), "unit": "GB/s", "cores": 1,
-        "kind": "oracle",
-        "sample": (f"full workload (1 sequence, 32 heads, {int(inp.context_lens[0])} tokens), "
-                   f"float64 numpy, 1 BLAS thread, best of {len(times)} runs "
-                   f"(median {sorted(times)[len(times) // 2] * 1e3:.2f} ms) in "
-                   f"{sum(times):.1f} s"),
-        "ms_per_step": round(best * 1e3, 3),
-    }
+    what = "full workload" if seqs is None else f"sequences {list(seqs)} of the workload"
+    desc = (f"{what}, float64 numpy, 1 BLAS thread, best of {len(times)} runs "
+            f"(median {sorted(times)[len(times) // 2] * 1e3:.2f} ms) in {sum(times):.1f} s")
+    return best, desc
+
+
+def graph_us(fn, n: int) -> float:
+    """Average device time per call of n calls captured in one HIP graph."""
+    import torch
+
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+def event_us(fn, n: int):
+    """Mean of per-call event intervals around n eager calls."""
+    import numpy as np
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([x.elapsed_time(y) * 1e3 for x, y in evs])
+    return float(t.mean()), t
+
+
+def causal_flops(inp) -> int:
+    """QK^T and PV multiply-adds of causal attention, 2 flops each."""
+    lens = inp.context_lens.tolist()
+    qs = inp.q_start.tolist()
+    total = 0
+    for s, length in enumerate(lens):
+        n_q = qs[s + 1] - qs[s]
+        past = length - n_q
+        keys = n_q * (past + 1) + n_q * (n_q - 1) // 2
+        total += 4 * inp.head_dim * keys * inp.num_q_heads
+    return total
 
 
 def main(argv=None) -> int:
@@ -138,7 +202,10 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
 
-    inp = wl.llama_decode(args.history)
+    if args.workload == "prefill":
+        return run_prefill(args, dev, props)
+    decode = args.workload == "decode"
+    inp = wl.llama_decode(args.history) if decode else wl.continuous_batching()
     kv_bytes = inp.kv_bytes()
     log(f"[bench] workload {inp.name}: {kv_bytes} KV bytes, pool {tuple(inp.k_pool.shape)}")
 
@@ -167,42 +234,11 @@ def main(argv=None) -> int:
     log(f"[bench] plan: blocks/split {plan.blocks_per_split}, splits {plan.max_splits}, "
         f"grid {grid}, combine wgs {comb}, workspace {plan.workspace_bytes} B")
 
-    def graph_us(fn, n: int) -> float:
-        """Average device time per call of n calls captured in one HIP graph."""
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(n):
-                fn(i)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
-
-    def event_us(fn, n: int):
-        """Mean of per-call event intervals around n eager calls."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        for i in range(n):
-            evs[i][0].record()
-            fn(i)
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        t = np.array([x.elapsed_time(y) * 1e3 for x, y in evs])
-        return float(t.mean()), t
-
     def step(i: int) -> None:
         c = i % copies
         binding.np_paged_attention_decode(desc, plan, q, kbig[c], vbig[c], bt, lens, out, ws)
 
-    if args.pmc_probe:
+    if args.pmc_probe and decode:
         for i in range(10):
             step(i)
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -216,6 +252,7 @@ def main(argv=None) -> int:
     # ---- parity gate (on copy 0) before any timing
     import oracle
 
+    log("[bench] parity gate against the oracle")
     step(0)
     torch.cuda.synchronize()
     ref = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
@@ -241,6 +278,8 @@ def main(argv=None) -> int:
     kernel_us, launch_us = event_us(step, K)
     log(f"[bench] per-launch events: mean {kernel_us:.3f} us, median "
         f"{float(np.median(launch_us)):.3f} us, min {float(launch_us.min()):.3f} us")
+    if not decode:
+        return report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies)
 
     # ---- reference kernels: the empty-kernel floor and a plain read of the
     # same number of bytes (cold, rotating over the same pool copies)
@@ -338,7 +377,133 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        best, sample = cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = {"value": round(kv_bytes / best / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle", "sample": sample,
+                               "ms_per_step": round(best * 1e3, 3)}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies) -> int:
+    kv_bytes = inp.kv_bytes()
+    gbs = kv_bytes / (us_per_step * 1e-6) / 1e9
+    rec = {
+        "metric": "paged-decode KV GB/s (% HBM peak), continuous batching",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(us_per_step / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "paged decode, continuous batching: 64 sequences, lengths uniform on "
+                        "[128, 8192], Llama-3.2-1B head shape, 40000-block pool, 1 layer",
+            "num_seqs": inp.num_seqs, "total_tokens": int(inp.context_lens.sum()),
+            "kv_bytes_per_step": kv_bytes, "blocks_per_split": plan.blocks_per_split,
+            "max_splits": plan.max_splits, "grid": list(grid),
+            "cache": f"{copies} pool copy of {2 * inp.k_pool.numel() * 2 >> 20} MiB (> MALL)",
+        },
+        "us_per_step": round(us_per_step, 3),
+        "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_kernel (bf16, d_pad 64, group 4, block 16)"},
+        "parity_max_abs_err": float(err.max()),
+        "device": props.name,
+    }
+    if not args.no_cpu_baseline:
+        seqs = [0, 1, 2, 3]
+        best, sample = cpu_baseline(inp, args.cpu_seconds, seqs=seqs)
+        sub_bytes = 2 * inp.num_kv_heads * inp.head_dim * 2 * int(inp.context_lens[seqs].sum())
+        rec["cpu_baseline"] = {"value": round(sub_bytes / best / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle", "sample": sample}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_prefill(args, dev, props) -> int:
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_178_amd import binding
+    from paged_kv_cache_178_amd import workloads as wl
+
+    inp = wl.chunked_prefill()
+    flops = causal_flops(inp)
+    log(f"[bench] workload {inp.name}: {flops} causal flops per step")
+    q = inp.q.to(dev)
+    bt = inp.block_table.to(dev)
+    lens = inp.context_lens.to(dev)
+    qst = inp.q_start.to(dev)
+    pool_bytes = 2 * inp.k_pool.numel() * inp.k_pool.element_size()
+    copies = 1 if args.warm else max(1, math.ceil(args.pool_bytes / pool_bytes))
+    kbig = inp.k_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+    vbig = inp.v_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+    out = torch.empty_like(q)
+    desc = binding.make_desc(q, kbig[0], bt, out=out, scale=inp.scale)
+    st = binding.np_check_paged_inputs(desc, q, kbig[0], vbig[0], bt, lens, out,
+                                       inp.block_table.numpy(), inp.context_lens.numpy(),
+                                       inp.q_start.numpy())
+    if st:
+        raise binding.NPError(st, "np_check_paged_inputs")
+    plan = binding.np_plan(desc, inp.context_lens.numpy(), inp.q_start.numpy())
+    grid, wg, _ = plan.launch_shape()
+    log(f"[bench] {copies} pool copies; grid {grid}")
+
+    def step(i: int) -> None:
+        c = i % copies
+        binding.np_paged_attention_prefill(desc, plan, q, kbig[c], vbig[c], bt, lens, qst, out)
+
+    if args.pmc_probe:
+        for i in range(5):
+            step(i)
+        torch.cuda.synchronize()
+        return 0
+    step(0)
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                 inp.context_lens, q_start=inp.q_start, scale=inp.scale)
+    err = np.abs(out.to("cpu", torch.float64).numpy() - ref)
+    if not (err <= 1e-2 + 1e-2 * np.abs(ref)).all():
+        print(f"bench.py: parity gate failed, max abs err {err.max():.3e}", file=sys.stderr)
+        return 1
+    log(f"[bench] parity gate passed: max abs err {err.max():.3e}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    us = graph_us(step, K)
+    tfs = flops / (us * 1e-6) / 1e12
+    log(f"[bench] graph: {K} steps -> {us:.3f} us/step, {tfs:.1f} TFLOP/s")
+    rec = {
+        "metric": "paged chunked-prefill TFLOP/s (% of dense bf16 MFMA peak)",
+        "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "chunked prefill over a paged cache: 4 sequences x (2048 cached + "
+                        "512 new rows), causal, Llama-3.2-1B head shape, 1 layer",
+            "causal_flops_per_step": flops, "grid": list(grid),
+            "cache": f"{copies} rotating pool copies",
+        },
+        "us_per_step": round(us, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tfs / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_prefill_kernel (bf16, d 64, block 16)"},
+        "parity_max_abs_err": float(err.max()),
+        "device": props.name,
+    }
+    if not args.no_cpu_baseline:
+        best, sample = cpu_baseline(inp, args.cpu_seconds, seqs=[0], prefill=True)
+        sub = wl.PagedInputs(**{**inp.__dict__, "context_lens": inp.context_lens[:1],
+                                "q_start": inp.q_start[:2]})
+        rec["cpu_baseline"] = {"value": round(causal_flops(sub) / best / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": sample}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
