@@ -192,6 +192,15 @@ __device__ __forceinline__ uint4 load16(const void* base, int64_t elem_off, int 
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem_off * elt);
 }
 
+// K/V rows are read exactly once per call: a nontemporal (streaming) load
+// keeps them from displacing reusable lines.
+__device__ __forceinline__ uint4 load16_stream(const void* base, int64_t elem_off, int elt) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+  const u32x4_t v = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(static_cast<const char*>(base) + elem_off * elt));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Split partials are published with agent-scope relaxed atomic stores and
 // read back with agent-scope relaxed atomic loads. On gfx950 these are plain
 // 64-bit global stores/loads with the device-coherence bit set, so the partials
@@ -396,8 +405,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
 
   // This wave's blocks are b0 + wave + i * NW. It takes them in groups of NG:
-  // all K/V loads of a group are issued before any of its blocks is used, and
-  // the table entries of the next group are read while this group computes.
+  // all K/V loads of a group are issued before any of its blocks is used, the
+  // loads of the next group are issued before this group computes, and table
+  // entries are read one group ahead of their loads.
   // The first group's entries are read before the context length is known
   // (table reads are clamped to the row, so they stay in bounds), which takes
   // one dependent memory round trip off the start of the kernel.
@@ -442,19 +452,96 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   const int ch_addr = chan_ok ? ch0 : p.head_dim - VEC;
   const int64_t head_off = int64_t(kvh) * p.kv_s2 + ch_addr + int64_t(row) * p.kv_s1;
 
-  for (int g0 = 0; g0 < nwb; g0 += NG) {
-    uint4 kr[NG][NLB], vr[NG][NLB];
+  // One group of NG blocks: pass 1 computes the scores of every slot of the
+  // group, the group max moves the running max once, pass 2 adds the weights
+  // and P.V.
+  auto compute_group = [&](const int g0, const uint4 (&kr)[NG][NLB], const uint4 (&vr)[NG][NLB]) {
+      // Pass 1: scores of every slot of the group (log2 units). Every block of
+      // the group is computed, so the group has a single path; a block past
+      // this wave's share gets a limit of 0, which masks all its slots (its
+      // loads were skipped and its registers are never used unmasked).
+      float sc[NG][NLB][G];
+  #pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int lim = g0 + i < nwb ? L : 0;
+        const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
+  #pragma unroll
+        for (int j = 0; j < NLB; ++j) {
+          const bool tok_ok = tok0 + j * TPL < lim;
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float dot = row_sum<LPR>(dot16<DT>(kr[i][j], qv[h], 0.0f));
+            sc[i][j][h] = tok_ok ? dot * p.scale_log2 : -INFINITY;
+          }
+        }
+      }
+      // One online-softmax step per group: the wave-wide max of the group's
+      // scores becomes the new reference; earlier sums are rescaled once.
+  #pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mx = sc[0][0][h];
+  #pragma unroll
+        for (int i = 0; i < NG; ++i)
+  #pragma unroll
+          for (int j = 0; j < NLB; ++j) mx = fmaxf(mx, sc[i][j][h]);
+        const float m_new = fmaxf(m[h], wave_max_rows<LPR>(mx));   // finite: block g0 is valid
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);   // 0 when m = -inf
+        m[h] = m_new;
+        l[h] *= alpha;
+  #pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
+      }
+      // Pass 2: weights and P.V.
+  #pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int lim = g0 + i < nwb ? L : 0;
+        const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
+        float w[NLB][G];
+  #pragma unroll
+        for (int j = 0; j < NLB; ++j)
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            w[j][h] = __builtin_amdgcn_exp2f(sc[i][j][h] - m[h]);   // 0 for masked slots
+            l[h] += w[j][h];
+          }
+        uint4 vv[NLB];
+  #pragma unroll
+        for (int j = 0; j < NLB; ++j) {
+          const bool tok_ok = tok0 + j * TPL < lim;
+          vv[j].x = tok_ok ? vr[i][j].x : 0u;
+          vv[j].y = tok_ok ? vr[i][j].y : 0u;
+          vv[j].z = tok_ok ? vr[i][j].z : 0u;
+          vv[j].w = tok_ok ? vr[i][j].w : 0u;
+        }
+        if constexpr (DT == NP_F32) {
+  #pragma unroll
+          for (int j = 0; j < NLB; ++j) {
+            float vf[VEC];
+            unpack16<DT>(vv[j], vf);
+  #pragma unroll
+            for (int h = 0; h < G; ++h)
+  #pragma unroll
+              for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(w[j][h], vf[e], acc[h][e]);
+          }
+        } else {
+  #pragma unroll
+          for (int j = 0; j < NLB; j += 2) pv_pair<DT, G, VEC>(vv[j], vv[j + 1], w, j, j + 1, acc);
+        }
+      }
+  };
+  auto load_group = [&](const int g0, uint4 (&kr)[NG][NLB], uint4 (&vr)[NG][NLB]) {
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       if (g0 + i < nwb) {
         const int64_t base = int64_t(ph[i]) * p.kv_s0 + head_off;
 #pragma unroll
         for (int j = 0; j < NLB; ++j) {
-          kr[i][j] = load16(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
-          vr[i][j] = load16(p.v, base + int64_t(j * TPL) * p.kv_s1, kElt);
+          kr[i][j] = load16_stream(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
+          vr[i][j] = load16_stream(p.v, base + int64_t(j * TPL) * p.kv_s1, kElt);
         }
       }
     }
+    // Table entries of the group after the one just issued.
     if (g0 + NG < nwb) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
@@ -462,78 +549,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
         ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
       }
     }
-    // Pass 1: scores of every slot of the group (log2 units). Every block of
-    // the group is computed, so the group has a single path; a block past
-    // this wave's share gets a limit of 0, which masks all its slots (its
-    // loads were skipped and its registers are never used unmasked).
-    float sc[NG][NLB][G];
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int lim = g0 + i < nwb ? L : 0;
-      const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
-#pragma unroll
-      for (int j = 0; j < NLB; ++j) {
-        const bool tok_ok = tok0 + j * TPL < lim;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float dot = row_sum<LPR>(dot16<DT>(kr[i][j], qv[h], 0.0f));
-          sc[i][j][h] = tok_ok ? dot * p.scale_log2 : -INFINITY;
-        }
-      }
-    }
-    // One online-softmax step per group: the wave-wide max of the group's
-    // scores becomes the new reference; earlier sums are rescaled once.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = sc[0][0][h];
-#pragma unroll
-      for (int i = 0; i < NG; ++i)
-#pragma unroll
-        for (int j = 0; j < NLB; ++j) mx = fmaxf(mx, sc[i][j][h]);
-      const float m_new = fmaxf(m[h], wave_max_rows<LPR>(mx));   // finite: block g0 is valid
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);   // 0 when m = -inf
-      m[h] = m_new;
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-    }
-    // Pass 2: weights and P.V.
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int lim = g0 + i < nwb ? L : 0;
-      const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
-      float w[NLB][G];
-#pragma unroll
-      for (int j = 0; j < NLB; ++j)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          w[j][h] = __builtin_amdgcn_exp2f(sc[i][j][h] - m[h]);   // 0 for masked slots
-          l[h] += w[j][h];
-        }
-      uint4 vv[NLB];
-#pragma unroll
-      for (int j = 0; j < NLB; ++j) {
-        const bool tok_ok = tok0 + j * TPL < lim;
-        vv[j].x = tok_ok ? vr[i][j].x : 0u;
-        vv[j].y = tok_ok ? vr[i][j].y : 0u;
-        vv[j].z = tok_ok ? vr[i][j].z : 0u;
-        vv[j].w = tok_ok ? vr[i][j].w : 0u;
-      }
-      if constexpr (DT == NP_F32) {
-#pragma unroll
-        for (int j = 0; j < NLB; ++j) {
-          float vf[VEC];
-          unpack16<DT>(vv[j], vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(w[j][h], vf[e], acc[h][e]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NLB; j += 2) pv_pair<DT, G, VEC>(vv[j], vv[j + 1], w, j, j + 1, acc);
-      }
-    }
+  };
+
+  // Software pipeline over groups with two register buffers: the loads of
+  // group g + 1 are in flight while group g computes.
+  uint4 ka[NG][NLB], va[NG][NLB], kb[NG][NLB], vb[NG][NLB];
+  if (nwb > 0) load_group(0, ka, va);
+  for (int g0 = 0; g0 < nwb; g0 += 2 * NG) {
+    if (g0 + NG < nwb) load_group(g0 + NG, kb, vb);
+    compute_group(g0, ka, va);
+    if (g0 + NG >= nwb) break;
+    if (g0 + 2 * NG < nwb) load_group(g0 + 2 * NG, ka, va);
+    compute_group(g0 + NG, kb, vb);
   }
 
   // ---- merge: rows of a wave share m, so their sums add directly; waves are
