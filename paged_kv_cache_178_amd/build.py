@@ -21,11 +21,18 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnp_paged.so")
 
 HIP_SOURCES = ["np_decode.hip", "np_prefill.hip", "np_probe.hip"]
+# Per-file flags. The prefill kernel masks by index with selects and never
+# relies on NaN propagation, so it is built without NaN semantics (max and min
+# lose their canonicalisation instructions).
+EXTRA_FLAGS = {"np_prefill.hip": ["-fno-honor-nans"]}
 HOST_SOURCES = ["np_host.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs (gfx950 has one register file), so the
+    # softmax reads scores and rescales outputs without AGPR copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 
@@ -58,7 +65,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        steps.append([hipcc, *HIPCC_FLAGS, *incs, "-c", os.path.join(CSRC, src), "-o", obj])
+        steps.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *incs, "-c",
+                      os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(steps)))) as ex:
         for res in ex.map(_run, steps):

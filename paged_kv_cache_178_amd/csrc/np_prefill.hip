@@ -40,6 +40,7 @@ namespace np {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;       // log2 units: weights stay below 256
 constexpr int kKT = 64;             // keys per staged tile
 constexpr int kD = 64;              // head_dim handled by this kernel
 constexpr int kKRow = kD + 8;       // K row pitch in LDS (elements): 144 bytes
@@ -87,6 +88,29 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
   else
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+}
+
+// l + the sum of the eight packed values of `x` (two per word), in fp32.
+template <int DT>
+__device__ __forceinline__ float sum_pairs(const uint4& x, float l) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (DT == NP_BF16)
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]),
+                                          __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+    else
+      l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[k]),
+                                 __builtin_bit_cast(f16x2_t, 0x3c003c00u), l, false);
+  }
+  return l;
+}
+
+// Scores are finite or -inf here (masked slots are set to -inf by index
+// before any max), so this file is built without NaN semantics and the max
+// needs no canonicalisation (it becomes v_max3_f32).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return fmaxf(a, fmaxf(b, c));
 }
 
 __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off) {
@@ -189,7 +213,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
     }
   };
 
-  float m = -INFINITY;   // running max of this lane's query (log2 units)
+  const float c = p.scale_log2;
+  float m = -INFINITY;   // running reference max of this lane's query (scaled, log2 units)
   float l = 0.0f;        // this lane's half of the running sum
   f32x16_t acc[kD / 32];
 #pragma unroll
@@ -217,46 +242,53 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
           st[b] = mfma<DT>(a, qreg[c], st[b]);
         }
       }
-      // Scale, mask (keys past this query's position or past the history),
-      // and the online-softmax step for this lane's query.
+      // Mask (keys past this query's position or past the history) on raw
+      // scores, then the online-softmax step for this lane's query. The
+      // running max m (scaled, log2 units) is lazy: it moves only when a score
+      // exceeds it by more than kLazy, decided for the whole wave by a ballot,
+      // so the cross-lane exchange and the rescale of acc are rare. Weights
+      // stay below 2^kLazy, well inside the input type's range.
       const int key_base = kt * kKT;
       const bool need_mask = key_base + kKT - 1 > past + q0 || key_base + kKT > L;
-      const int q_pos = past + my_q;
-      float mx = -INFINITY;
+      if (need_mask) {
+        // Last visible key of this row: past + row, and never past the history
+        // (rows past the chunk end only exist as padding).
+        const int lim = min(past + my_q, L - 1) - key_base - 4 * half;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = st[b][i] * p.scale_log2;
-          if (need_mask) {
-            const int key = key_base + 32 * b + 8 * (i / 4) + 4 * half + (i % 4);
-            x = (key <= q_pos && key < L) ? x : -INFINITY;
-          }
-          st[b][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);            // finite: key 0 is visible to every row
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      l *= alpha;
+          for (int i = 0; i < 16; ++i)
+            st[b][i] = 32 * b + 8 * (i / 4) + (i % 4) <= lim ? st[b][i] : -INFINITY;
+      }
+      float mxr = max3(st[0][0], st[1][0], st[0][1]);
+      mxr = max3(mxr, st[1][1], st[0][2]);
 #pragma unroll
-      for (int cb = 0; cb < kD / 32; ++cb)
+      for (int i = 2; i < 15; ++i) mxr = max3(mxr, st[1][i], st[0][i + 1]);
+      mxr = max3(mxr, st[1][15], st[1][15]);
+      if (__ballot(mxr * c > m + kLazy)) {
+        const float mx = fmaxf(mxr, __shfl_xor(mxr, 32)) * c;   // same for the lane pair
+        const bool move = mx > m + kLazy;                       // first tile: m = -inf
+        const float alpha = move ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
+        m = move ? mx : m;
+        l *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+        for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+      }
       // P^T in the input type, packed for the B operand: k-step ks uses the
-      // registers 8(ks%2) .. 8(ks%2)+7 of half ks/2.
+      // registers 8(ks%2) .. 8(ks%2)+7 of half ks/2. The row sum adds the same
+      // rounded weights the product uses (v_dot2 against (1, 1)).
       uint4 pb[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         float e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(st[ks / 2][8 * (ks % 2) + j] - m);
-          l += e[j];
-        }
+        for (int j = 0; j < 8; ++j)
+          e[j] = __builtin_amdgcn_exp2f(fmaf(st[ks / 2][8 * (ks % 2) + j], c, -m));
         pb[ks] = make_uint4(pack2<DT>(e[0], e[1]), pack2<DT>(e[2], e[3]),
                             pack2<DT>(e[4], e[5]), pack2<DT>(e[6], e[7]));
+        l = sum_pairs<DT>(pb[ks], l);
       }
       // O^T += V^T P^T. Register j of k-step ks holds key
       // 16 ks + 8 (j / 4) + 4 half + j % 4 of the tile; V^T is read in that order.
