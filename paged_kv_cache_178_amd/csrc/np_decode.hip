@@ -408,16 +408,30 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   // all K/V loads of a group are issued before any of its blocks is used, the
   // loads of the next group are issued before this group computes, and table
   // entries are read one group ahead of their loads.
-  // The first group's entries are read before the context length is known
-  // (table reads are clamped to the row, so they stay in bounds), which takes
-  // one dependent memory round trip off the start of the kernel.
+  // The first group's entries and this head group's q are read before the
+  // context length is known (table reads are clamped to the row, q reads to
+  // the real channels), so these reads share one memory round trip.
   int ph[NG];
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int b = b0 + wave + i * NW;
     ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
   }
+  // q chunks of the G heads of this group. Padded channels load the last
+  // real chunk and are zeroed by a select, so every lane loads.
+  const int q_ch = chan_ok ? ch0 : p.head_dim - VEC;
+  uint4 qv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 t = load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + q_ch, kElt);
+    qv[h] = chan_ok ? t : make_uint4(0, 0, 0, 0);
+  }
   const int L = p.lens[s];
+  // The table entries are needed only past the exit test below; tying them to
+  // this point keeps the compiler from moving their reads after it (which
+  // would add a second round trip before the first K/V load).
+#pragma unroll
+  for (int i = 0; i < NG; ++i) asm volatile("" ::"s"(ph[i]));
   int nb = (L + BS - 1) / BS;
   nb = nb < p.max_blocks ? nb : p.max_blocks;
   int splits = (nb + p.bps - 1) / p.bps;
@@ -425,15 +439,6 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   if (split >= splits) return;
   const int b1 = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
   const int nwb = (b1 - b0 - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
-
-  // q chunks of the G heads of this group (zero in padded channels).
-  uint4 qv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    qv[h] = make_uint4(0, 0, 0, 0);
-    if (chan_ok)
-      qv[h] = load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + ch0, kElt);
-  }
 
   // Online-softmax state. m[h] is shared by the whole wave (wave-uniform);
   // l[h] and acc[h][.] are this lane's partial sums over the slots it saw.
@@ -449,8 +454,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   // Loads are unconditional inside a valid block: slots past the history are
   // still inside the block, and padded channels read the last real chunk
   // instead; both are masked by selects below, never by multiplication.
-  const int ch_addr = chan_ok ? ch0 : p.head_dim - VEC;
-  const int64_t head_off = int64_t(kvh) * p.kv_s2 + ch_addr + int64_t(row) * p.kv_s1;
+  const int64_t head_off = int64_t(kvh) * p.kv_s2 + q_ch + int64_t(row) * p.kv_s1;
 
   // One group of NG blocks: pass 1 computes the scores of every slot of the
   // group, the group max moves the running max once, pass 2 adds the weights
