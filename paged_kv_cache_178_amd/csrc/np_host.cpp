@@ -250,14 +250,15 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     }
   } else {
     // Chunked prefill: one workgroup per (sequence, KV head, tile). A tile is
-    // kPrefillWaves units; a unit is one query head of the group times
-    // kPrefillRowsPerWave query rows. Units are numbered head-fastest.
+    // kPrefillUnits units; a unit is one query head of the group times
+    // kPrefillRowsPerWave query rows. Units are numbered head-fastest. Each
+    // unit has two waves, which take alternate key tiles.
     int64_t max_tiles = 0;
     std::vector<int64_t> tiles(c.num_seqs);
     for (int32_t s = 0; s < c.num_seqs; ++s) {
       const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
       const int64_t units = c.group * ceil_div(n_q, kPrefillRowsPerWave);
-      tiles[s] = ceil_div(units, kPrefillWaves);
+      tiles[s] = ceil_div(units, kPrefillUnits);
       max_tiles = std::max(max_tiles, tiles[s]);
     }
     c.blocks_per_split = 0;
@@ -276,8 +277,8 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
         const int64_t tile = x / c.hkv, kvh = x % c.hkv;
         if (tile >= tiles[s]) continue;
         // Rows covered by the tile's units (clipped to the chunk).
-        const int64_t u0 = tile * kPrefillWaves;
-        const int64_t u1 = std::min<int64_t>(u0 + kPrefillWaves,
+        const int64_t u0 = tile * kPrefillUnits;
+        const int64_t u1 = std::min<int64_t>(u0 + kPrefillUnits,
                                              c.group * ceil_div(n_q, kPrefillRowsPerWave));
         const int64_t r0 = (u0 / c.group) * kPrefillRowsPerWave;
         const int64_t r1 = std::min<int64_t>(((u1 - 1) / c.group + 1) * kPrefillRowsPerWave, n_q);

@@ -13,8 +13,9 @@ namespace np {
 constexpr uint32_t kPlanMagic = 0x4e50504cu;   // "NPPL"
 constexpr int kWaveSize = 64;
 constexpr int kDecodeWaves = 4;                // waves per decode workgroup
-constexpr int kPrefillWaves = 4;               // waves per prefill workgroup
-constexpr int kPrefillRowsPerWave = 32;        // query rows of one head per wave
+constexpr int kPrefillUnits = 4;               // (head, query rows) units per prefill workgroup
+constexpr int kPrefillWaves = 8;               // waves per prefill workgroup: two per unit
+constexpr int kPrefillRowsPerWave = 64;        // query rows of one head per wave
 constexpr int kMaxGroup = 8;                   // largest Hq/Hkv with a kernel
 constexpr size_t kWsAlign = 256;
 constexpr int kCounterStride = 64;             // uint32 words between arrival counters

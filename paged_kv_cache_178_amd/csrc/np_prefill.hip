@@ -45,7 +45,7 @@ constexpr int kKT = 64;             // keys per staged tile
 constexpr int kD = 64;              // head_dim handled by this kernel
 constexpr int kKRow = kD + 8;       // K row pitch in LDS (elements): 144 bytes
 constexpr int kVRow = kKT + 4;      // V^T row pitch in LDS (elements): 136 bytes
-constexpr int kRows = kPrefillRowsPerWave;   // 32 query rows per unit
+constexpr int kRows = kPrefillRowsPerWave;   // query rows per unit (two MFMA column blocks)
 
 struct PrefillParams {
   const void* q;
@@ -121,10 +121,15 @@ template <int DT, int BS>
 __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kernel(
     const PrefillParams p) {
   static_assert(BS == 16, "a wave stages one 16-slot block per key tile");
-  constexpr int NW = kPrefillWaves;
-  static_assert(NW * BS == kKT, "one block per wave per key tile");
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kD * kVRow];
+  constexpr int NU = kPrefillUnits;       // units (and waves per group)
+  constexpr int NG = kPrefillWaves / NU;  // wave groups, taking alternate key tiles
+  static_assert(NG == 2 && NU * BS == kKT, "two groups; one block per wave per tile");
+  constexpr int QB = kRows / 32;          // 32-query column blocks per wave
+  static_assert(QB == 2, "the step below pairs two query blocks");
+  // Double-buffered pairs of key tiles (tile 2j + g is group g's in step j).
+  constexpr int kKTile = kKT * kKRow, kVTile = kD * kVRow;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][NG][kKTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][NG][kVTile];
 
   const int kvh = blockIdx.x % p.hkv;
   const int tile = blockIdx.x / p.hkv;
@@ -136,192 +141,284 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   const int past = L - n_q;
   const int nqb = (n_q + kRows - 1) / kRows;
   const int units = G * nqb;
-  if (tile * NW >= units) return;
+  if (tile * NU >= units) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int grp = wave / NU;           // key tiles grp, grp + 2, grp + 4, ...
+  const int wu = wave % NU;            // unit within the workgroup
   const int lane = threadIdx.x % kWaveSize;
   const int half = lane / 32;          // which 8 of a 16-wide k-step this lane feeds
-  const int col = lane % 32;           // this lane's query row within the unit
+  const int col = lane % 32;           // this lane's query column within a block
 
-  // This wave's unit (head, 32-row query block); idle waves still stage K/V.
-  const int unit = tile * NW + wave;
+  // This wave's unit (head, 64-row query block); idle units' waves still stage K/V.
+  const int unit = tile * NU + wu;
   const bool active = unit < units;
   const int h = active ? unit % G : 0;
   const int q0 = active ? (unit / G) * kRows : 0;
-  // Last key any row of this wave sees, and of the whole workgroup.
+  // Last key any row of this unit sees, and of the whole workgroup.
   const int q_last = (q0 + kRows < n_q ? q0 + kRows : n_q) - 1;
-  const int wave_last_key = active ? past + q_last : -1;
-  int wg_last_unit = tile * NW + NW - 1;
+  const int unit_last_key = active ? past + q_last : -1;
+  int wg_last_unit = tile * NU + NU - 1;
   wg_last_unit = wg_last_unit < units ? wg_last_unit : units - 1;
   const int wg_q_last_blk = wg_last_unit / G;
   const int wg_q_last = ((wg_q_last_blk + 1) * kRows < n_q ? (wg_q_last_blk + 1) * kRows : n_q) - 1;
   const int n_tiles = (past + wg_q_last) / kKT + 1;
-  const int wave_tiles = active ? wave_last_key / kKT + 1 : 0;
+  const int n_steps = (n_tiles + NG - 1) / NG;
+  const int unit_tiles = active ? unit_last_key / kKT + 1 : 0;
 
-  // Query rows of this lane in the four 16-channel k-chunks (B operand of S^T).
-  const int my_q = q0 + col;
-  const bool q_ok = active && my_q < n_q;
-  uint4 qreg[kD / 16];
-  {
-    const int64_t qoff = int64_t(row0 + (q_ok ? my_q : 0)) * p.q_s0 +
+  // This lane's two queries (one per column block), in the four 16-channel
+  // k-chunks (B operand of S^T).
+  int my_q[QB];
+  bool q_ok[QB];
+  uint4 qreg[QB][kD / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    my_q[qb] = q0 + 32 * qb + col;
+    q_ok[qb] = active && my_q[qb] < n_q;
+    const int64_t qoff = int64_t(row0 + (q_ok[qb] ? my_q[qb] : 0)) * p.q_s0 +
                          int64_t(kvh * G + h) * p.q_s1 + 8 * half;
 #pragma unroll
     for (int c = 0; c < kD / 16; ++c)
-      qreg[c] = q_ok ? ld16(p.q, qoff + 16 * c) : make_uint4(0, 0, 0, 0);
+      qreg[qb][c] = q_ok[qb] ? ld16(p.q, qoff + 16 * c) : make_uint4(0, 0, 0, 0);
   }
 
-  // Staging map: wave w stages block w of the key tile; lane (kp, cc) holds
-  // slots 2kp, 2kp+1 of that block, channels 8cc .. 8cc+7.
+  // Staging map: in step j, wave w stages block w % NU of tile 2j + w / NU;
+  // lane (kp, cc) holds slots 2kp, 2kp+1 of that block, channels 8cc .. 8cc+7.
   const int kp = lane / 8;
   const int cc = lane % 8;
   const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
   int nb = (L + BS - 1) / BS;
   nb = nb < p.max_blocks ? nb : p.max_blocks;
   uint4 kst[2], vst[2];
-  auto stage_load = [&](int kt) {
-    const int blk = kt * NW + wave;
-    if (blk < nb) {
-      const int64_t base = int64_t(bt_row[blk]) * p.kv_s0 + int64_t(kvh) * p.kv_s2 + 8 * cc +
-                           int64_t(2 * kp) * p.kv_s1;
-      kst[0] = ld16(p.k, base);
-      kst[1] = ld16(p.k, base + p.kv_s1);
-      vst[0] = ld16(p.v, base);
-      vst[1] = ld16(p.v, base + p.kv_s1);
-    }
+  // Loads are unconditional: a block past the history (or a tile past the
+  // last) reads the last real block instead, and what it stages is never used
+  // unmasked.
+  auto stage_load = [&](int j) {
+    int blk = (NG * j + grp) * NU + wu;
+    blk = blk < nb ? blk : nb - 1;
+    const int64_t base = int64_t(bt_row[blk]) * p.kv_s0 + int64_t(kvh) * p.kv_s2 + 8 * cc +
+                         int64_t(2 * kp) * p.kv_s1;
+    kst[0] = ld16(p.k, base);
+    kst[1] = ld16(p.k, base + p.kv_s1);
+    vst[0] = ld16(p.v, base);
+    vst[1] = ld16(p.v, base + p.kv_s1);
   };
-  auto stage_store = [&](int kt, int buf) {
-    const int blk = kt * NW + wave;
-    const int key0 = wave * BS + 2 * kp;            // key index within the tile
-    const int t0 = kt * kKT + key0;                 // absolute key of slot 2kp
+  auto stage_store = [&](int j) {
+    const int blk = (NG * j + grp) * NU + wu;
+    uint16_t* kl = k_lds[j % 2][grp];
+    uint16_t* vl = vt_lds[j % 2][grp];
+    const int key0 = wu * BS + 2 * kp;              // key index within the tile
+    const int t0 = blk * BS + 2 * kp;               // absolute key of slot 2kp
     // V rows of keys past the history are zero (their weight is 0 and 0 * V
     // must not turn into NaN); K rows there are masked by score selects.
     const bool ok0 = blk < nb && t0 < L;
     const bool ok1 = blk < nb && t0 + 1 < L;
-    *reinterpret_cast<uint4*>(&k_lds[buf][key0 * kKRow + 8 * cc]) = kst[0];
-    *reinterpret_cast<uint4*>(&k_lds[buf][(key0 + 1) * kKRow + 8 * cc]) = kst[1];
+    *reinterpret_cast<uint4*>(&kl[key0 * kKRow + 8 * cc]) = kst[0];
+    *reinterpret_cast<uint4*>(&kl[(key0 + 1) * kKRow + 8 * cc]) = kst[1];
     const uint32_t a[4] = {ok0 ? vst[0].x : 0u, ok0 ? vst[0].y : 0u, ok0 ? vst[0].z : 0u,
                            ok0 ? vst[0].w : 0u};
     const uint32_t b[4] = {ok1 ? vst[1].x : 0u, ok1 ? vst[1].y : 0u, ok1 ? vst[1].z : 0u,
                            ok1 ? vst[1].w : 0u};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // channel 8cc + 2j: low halves; channel 8cc + 2j + 1: high halves.
-      *reinterpret_cast<uint32_t*>(&vt_lds[buf][(8 * cc + 2 * j) * kVRow + key0]) =
-          __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(&vt_lds[buf][(8 * cc + 2 * j + 1) * kVRow + key0]) =
-          __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+    for (int jj = 0; jj < 4; ++jj) {
+      // channel 8cc + 2jj: low halves; channel 8cc + 2jj + 1: high halves.
+      *reinterpret_cast<uint32_t*>(&vl[(8 * cc + 2 * jj) * kVRow + key0]) =
+          __builtin_amdgcn_perm(b[jj], a[jj], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&vl[(8 * cc + 2 * jj + 1) * kVRow + key0]) =
+          __builtin_amdgcn_perm(b[jj], a[jj], 0x07060302u);
     }
   };
 
   const float c = p.scale_log2;
-  float m = -INFINITY;   // running reference max of this lane's query (scaled, log2 units)
-  float l = 0.0f;        // this lane's half of the running sum
-  f32x16_t acc[kD / 32];
+  float m[QB], l[QB];          // running reference max (scaled, log2 units); lane's half-sum
+  f32x16_t acc[QB][kD / 32];   // O^T column blocks
 #pragma unroll
-  for (int cb = 0; cb < kD / 32; ++cb) acc[cb] = f32x16_t{};
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < kD / 32; ++cb) acc[qb][cb] = f32x16_t{};
+  }
 
-  stage_load(0);
-  stage_store(0, 0);
-  if (n_tiles > 1) stage_load(1);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt < wave_tiles) {
-      const uint16_t* kl = k_lds[buf];
-      const uint16_t* vl = vt_lds[buf];
-      // S^T for the two 32-key halves of the tile.
-      f32x16_t st[2];
+  // Mask (keys past the query's position or past the history) on raw scores
+  // and take the online-softmax step up to the rescale. The running max m
+  // (scaled, log2 units) is lazy: it moves only when a score exceeds it by
+  // more than kLazy, decided for the whole wave by a ballot, so the
+  // cross-lane exchange and the rescale of acc are rare. Weights stay below
+  // 2^kLazy, well inside the input type's range.
+  auto softmax_head = [&](int kt, int qb, f32x16_t (&st)[2]) {
+    const int key_base = kt * kKT;
+    const bool need_mask = key_base + kKT - 1 > past + q0 + 32 * qb || key_base + kKT > L;
+    if (need_mask) {
+      // Last visible key of this row: past + row, and never past the history
+      // (rows past the chunk end only exist as padding).
+      const int lim = min(past + my_q[qb], L - 1) - key_base - 4 * half;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        st[b] = f32x16_t{};
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int c = 0; c < kD / 16; ++c) {
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(&kl[(32 * b + col) * kKRow + 16 * c + 8 * half]);
-          st[b] = mfma<DT>(a, qreg[c], st[b]);
-        }
-      }
-      // Mask (keys past this query's position or past the history) on raw
-      // scores, then the online-softmax step for this lane's query. The
-      // running max m (scaled, log2 units) is lazy: it moves only when a score
-      // exceeds it by more than kLazy, decided for the whole wave by a ballot,
-      // so the cross-lane exchange and the rescale of acc are rare. Weights
-      // stay below 2^kLazy, well inside the input type's range.
-      const int key_base = kt * kKT;
-      const bool need_mask = key_base + kKT - 1 > past + q0 || key_base + kKT > L;
-      if (need_mask) {
-        // Last visible key of this row: past + row, and never past the history
-        // (rows past the chunk end only exist as padding).
-        const int lim = min(past + my_q, L - 1) - key_base - 4 * half;
+        for (int i = 0; i < 16; ++i)
+          st[b][i] = 32 * b + 8 * (i / 4) + (i % 4) <= lim ? st[b][i] : -INFINITY;
+    }
+    float mxr = max3(st[0][0], st[1][0], st[0][1]);
+    mxr = max3(mxr, st[1][1], st[0][2]);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            st[b][i] = 32 * b + 8 * (i / 4) + (i % 4) <= lim ? st[b][i] : -INFINITY;
-      }
-      float mxr = max3(st[0][0], st[1][0], st[0][1]);
-      mxr = max3(mxr, st[1][1], st[0][2]);
-#pragma unroll
-      for (int i = 2; i < 15; ++i) mxr = max3(mxr, st[1][i], st[0][i + 1]);
-      mxr = max3(mxr, st[1][15], st[1][15]);
-      if (__ballot(mxr * c > m + kLazy)) {
-        const float mx = fmaxf(mxr, __shfl_xor(mxr, 32)) * c;   // same for the lane pair
-        const bool move = mx > m + kLazy;                       // first tile: m = -inf
-        const float alpha = move ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
-        m = move ? mx : m;
-        l *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < kD / 32; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-      }
-      // P^T in the input type, packed for the B operand: k-step ks uses the
-      // registers 8(ks%2) .. 8(ks%2)+7 of half ks/2. The row sum adds the same
-      // rounded weights the product uses (v_dot2 against (1, 1)).
-      uint4 pb[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          e[j] = __builtin_amdgcn_exp2f(fmaf(st[ks / 2][8 * (ks % 2) + j], c, -m));
-        pb[ks] = make_uint4(pack2<DT>(e[0], e[1]), pack2<DT>(e[2], e[3]),
-                            pack2<DT>(e[4], e[5]), pack2<DT>(e[6], e[7]));
-        l = sum_pairs<DT>(pb[ks], l);
-      }
-      // O^T += V^T P^T. Register j of k-step ks holds key
-      // 16 ks + 8 (j / 4) + 4 half + j % 4 of the tile; V^T is read in that order.
+    for (int i = 2; i < 15; ++i) mxr = max3(mxr, st[1][i], st[0][i + 1]);
+    mxr = max3(mxr, st[1][15], st[1][15]);
+    if (__ballot(mxr * c > m[qb] + kLazy)) {
+      const float mx = fmaxf(mxr, __shfl_xor(mxr, 32)) * c;   // same for the lane pair
+      const bool move = mx > m[qb] + kLazy;                   // first tile: m = -inf
+      const float alpha = move ? __builtin_amdgcn_exp2f(m[qb] - mx) : 1.0f;
+      m[qb] = move ? mx : m[qb];
+      l[qb] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < kD / 32; ++cb)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const uint16_t* vrow = &vl[(32 * cb + col) * kVRow + 16 * ks + 4 * half];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          acc[cb] = mfma<DT>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], acc[cb]);
-        }
+        for (int i = 0; i < 16; ++i) acc[qb][cb][i] *= alpha;
     }
-    if (kt + 1 < n_tiles) {
-      stage_store(kt + 1, buf ^ 1);
-      if (kt + 2 < n_tiles) stage_load(kt + 2);
+  };
+  // P^T in the input type, packed for the B operand: k-step ks uses the
+  // registers 8(ks%2) .. 8(ks%2)+7 of half ks/2. The row sum adds the same
+  // rounded weights the product uses (v_dot2 against (1, 1)).
+  // A lane whose scores so far were all masked still has m = -inf (a wave
+  // group may start on a tile that some of its rows cannot see): its weights
+  // must be 0, not exp2(-inf + inf).
+  auto weights = [&](int qb, int ks, const f32x16_t (&st)[2], uint4 (&pb)[4]) {
+    const float neg_m = m[qb] == -INFINITY ? 0.0f : -m[qb];
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      e[j] = __builtin_amdgcn_exp2f(fmaf(st[ks / 2][8 * (ks % 2) + j], c, neg_m));
+    pb[ks] = make_uint4(pack2<DT>(e[0], e[1]), pack2<DT>(e[2], e[3]),
+                        pack2<DT>(e[4], e[5]), pack2<DT>(e[6], e[7]));
+    l[qb] = sum_pairs<DT>(pb[ks], l[qb]);
+    // Pin the weights here: without a use at this point the compiler sinks
+    // their computation to the P.V that reads them, undoing the interleave.
+    asm volatile("" ::"v"(pb[ks].x), "v"(pb[ks].y), "v"(pb[ks].z), "v"(pb[ks].w), "v"(l[qb]));
+  };
+
+  // One key tile of this wave. Matrix-core work is paired with independent
+  // VALU work in chunks whose order scheduling barriers fix (an MFMA runs for
+  // many cycles after it issues; the instructions after it, of this wave or of
+  // the other wave on the SIMD, issue meanwhile):
+  //   S^T of block 0
+  //   softmax weights of block 0  | S^T of block 1
+  //   softmax weights of block 1  | P.V of block 0
+  //   P.V of block 1
+  // Register j of k-step ks of P^T holds key 16 ks + 8 (j / 4) + 4 half + j % 4
+  // of the tile; V^T is read in that order.
+  auto tile_step = [&](int kt, const uint16_t* kl, const uint16_t* vl) {
+    uint4 ka[2][kD / 16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int k = 0; k < kD / 16; ++k)
+        ka[b][k] = *reinterpret_cast<const uint4*>(&kl[(32 * b + col) * kKRow + 16 * k + 8 * half]);
+    f32x16_t s0[2], s1[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s0[b] = f32x16_t{};
+#pragma unroll
+      for (int k = 0; k < kD / 16; ++k) s0[b] = mfma<DT>(ka[b][k], qreg[0][k], s0[b]);
     }
+    softmax_head(kt, 0, s0);
+    uint4 pb0[4], pb1[4];
+    s1[0] = f32x16_t{};
+    s1[1] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s1[0] = mfma<DT>(ka[0][ks], qreg[1][ks], s1[0]);
+      s1[1] = mfma<DT>(ka[1][ks], qreg[1][ks], s1[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      weights(0, ks, s0, pb0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint4 va[kD / 32][4];
+#pragma unroll
+    for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint16_t* vrow = &vl[(32 * cb + col) * kVRow + 16 * ks + 4 * half];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        va[cb][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    softmax_head(kt, 1, s1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int cb = 0; cb < kD / 32; ++cb) acc[0][cb] = mfma<DT>(va[cb][ks], pb0[ks], acc[0][cb]);
+      __builtin_amdgcn_sched_barrier(0);
+      weights(1, ks, s1, pb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int cb = 0; cb < kD / 32; ++cb) acc[1][cb] = mfma<DT>(va[cb][ks], pb1[ks], acc[1][cb]);
+  };
+
+  // Step j: group g takes tile 2j + g from buffer j % 2 while every wave
+  // stages step j + 1 into the other buffer; one barrier per step.
+  stage_load(0);
+  stage_store(0);
+  stage_load(1);
+  __syncthreads();
+  for (int j = 0; j < n_steps; ++j) {
+    const int kt = NG * j + grp;
+    if (kt < unit_tiles) tile_step(kt, k_lds[j % 2][grp], vt_lds[j % 2][grp]);
+    stage_store(j + 1);
+    stage_load(j + 2);
     __syncthreads();
   }
 
-  if (!q_ok) return;
-  const float l_tot = l + __shfl_xor(l, 32);
-  const float r = 1.0f / l_tot;
-  const int64_t obase = int64_t(row0 + my_q) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1;
+  // Merge the two groups' states of each unit through LDS (the staging
+  // buffers are free now), one query block at a time: group 1 writes, group 0
+  // combines and stores.
+  float* xa = reinterpret_cast<float*>(&k_lds[0][0][0]);      // [NU][kD/32][16][64]
+  float* xm = reinterpret_cast<float*>(&vt_lds[0][0][0]);     // [NU][2][64]
+  static_assert(NU * (kD / 32) * 16 * kWaveSize * 4 <= sizeof(k_lds), "merge space");
+  static_assert(NU * 2 * kWaveSize * 4 <= sizeof(vt_lds), "merge space");
 #pragma unroll
-  for (int cb = 0; cb < kD / 32; ++cb)
+  for (int qb = 0; qb < QB; ++qb) {
+    if (grp == 1) {
+      xm[(wu * 2 + 0) * kWaveSize + lane] = m[qb];
+      xm[(wu * 2 + 1) * kWaveSize + lane] = l[qb];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ch = 32 * cb + 8 * g + 4 * half;
-      const uint2 v = make_uint2(pack2<DT>(acc[cb][4 * g] * r, acc[cb][4 * g + 1] * r),
-                                 pack2<DT>(acc[cb][4 * g + 2] * r, acc[cb][4 * g + 3] * r));
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + ch) = v;
+      for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          xa[((wu * (kD / 32) + cb) * 16 + i) * kWaveSize + lane] = acc[qb][cb][i];
     }
+    __syncthreads();
+    if (grp == 0 && q_ok[qb]) {
+      const float m1 = xm[(wu * 2 + 0) * kWaveSize + lane];
+      const float l1 = xm[(wu * 2 + 1) * kWaveSize + lane];
+      // m is shared by a lane pair (both halves of a query) and so is m1.
+      const float mm = fmaxf(m[qb], m1);
+      const float a0 = __builtin_amdgcn_exp2f(m[qb] - mm);   // 0 for a group that saw nothing
+      const float a1 = __builtin_amdgcn_exp2f(m1 - mm);
+      const float lh = l[qb] * a0 + l1 * a1;
+      const float l_tot = lh + __shfl_xor(lh, 32);
+      const float r = 1.0f / l_tot;
+      const int64_t obase = int64_t(row0 + my_q[qb]) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1;
+#pragma unroll
+      for (int cb = 0; cb < kD / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g + e;
+            const float x1 = xa[((wu * (kD / 32) + cb) * 16 + i) * kWaveSize + lane];
+            o[e] = (acc[qb][cb][i] * a0 + x1 * a1) * r;
+          }
+          const int ch = 32 * cb + 8 * g + 4 * half;
+          const uint2 v = make_uint2(pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3]));
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + ch) = v;
+        }
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace

@@ -155,7 +155,7 @@ def model_decode_plan(lens, bs, hkv, num_cus=256, wgs_per_cu=1, min_bps=4, max_b
     return bps, max_splits, items
 
 
-def model_prefill_plan(q_start, hq, hkv, rows=32, waves=4):
+def model_prefill_plan(q_start, hq, hkv, rows=64, waves=4):
     g = hq // hkv
     n_qs = [q_start[i + 1] - q_start[i] for i in range(len(q_start) - 1)]
     tiles = [math.ceil(g * math.ceil(n / rows) / waves) for n in n_qs]
@@ -268,11 +268,11 @@ def test_prefill_plan_matches_model(seed):
     max_tiles, items = model_prefill_plan(q_start.tolist(), hkv * g, hkv)
     assert plan.work_items() == items
     grid, wg, comb = plan.launch_shape()
-    assert grid == (max_tiles * hkv, num_seqs, 1) and wg == 256 and comb == 0
+    assert grid == (max_tiles * hkv, num_seqs, 1) and wg == 512 and comb == 0
     assert plan.workspace_bytes == 0
     # Every (seq, head, query row) unit is in exactly one tile.
     for s in range(num_seqs):
-        units = g * math.ceil(n_q[s] / 32)
+        units = g * math.ceil(n_q[s] / 64)
         tiles = {it[2] for it in items if it[0] == s and it[1] == 0}
         assert tiles == set(range(math.ceil(units / 4)))
 
