@@ -188,6 +188,38 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// Sum of N values (N a multiple of 4) over the 8 rows of a wave whose rows
+// are 8 lanes wide (lane bits 3..5). Bit 3 is a DPP row rotate; bits 4 and 5
+// use the gfx950 lane swaps, each of which exchanges half of two registers
+// between lane groups, so one swap and one add reduce two values at once and
+// leave them interleaved. On return u[k] holds, in 16-lane group r, value
+// 4k + r summed over all 8 rows (lanes i and i ^ 8 hold the same sums).
+template <int N>
+__device__ __forceinline__ void rows8_sum(float (&v)[N], float (&u)[N / 4]) {
+  static_assert(N % 4 == 0, "values come in fours");
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f<0x128>(v[k]);   // row_ror:8 (lane i <-> i^8)
+  float w[N / 2];
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[2 * j]),
+                                                    __builtin_bit_cast(uint32_t, v[2 * j + 1]),
+                                                    false, false);
+    // (Elements copied out first: a bit cast applied to the subscripted
+    // result reads element 0 twice with this compiler.)
+    const uint32_t r0 = r[0], r1 = r[1];
+    w[j] = __uint_as_float(r0) + __uint_as_float(r1);
+  }
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, w[2 * k]),
+                                                    __builtin_bit_cast(uint32_t, w[2 * k + 1]),
+                                                    false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    u[k] = __uint_as_float(r0) + __uint_as_float(r1);
+  }
+}
+
 __device__ __forceinline__ uint4 load16(const void* base, int64_t elem_off, int elt) {
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem_off * elt);
 }
@@ -569,17 +601,57 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 
   // ---- merge: rows of a wave share m, so their sums add directly; waves are
   // weighted by 2^(m_wave - M). One barrier.
-  __shared__ float red_acc[NW][TPL][G][D_PAD];
-  __shared__ float red_l[NW][TPL][G];
+  // The per-wave row sums (TPL rows) are formed in registers where the row
+  // count is 8 (16-bit types, d_pad 64): partner rows are one DPP step and two
+  // lane-swap steps apart, and each swap step halves the values a lane holds
+  // (the transposed reduction), so LDS carries one partial per wave instead of
+  // one per row.
+  constexpr bool kRowsInRegs = LPR == 8;
+  constexpr int NRW = kRowsInRegs ? 1 : TPL;   // partials per wave in LDS
+  __shared__ float red_acc[NW][NRW][G][D_PAD];
+  __shared__ float red_l[NW][NRW][G];
   __shared__ float red_m[NW][G];
+  if constexpr (kRowsInRegs) {
+    constexpr int N = G * VEC;                   // a multiple of 4
+    constexpr int NL = (G + 3) / 4 * 4;
+    float v[N], lv[NL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < VEC; e += 4)
-      *reinterpret_cast<float4*>(&red_acc[wave][row][h][ch0 + e]) =
-          make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
-    if (lane % LPR == 0) red_l[wave][row][h] = l[h];
-    if (lane == 0) red_m[wave][h] = m[h];
+      for (int e = 0; e < VEC; ++e) v[h * VEC + e] = acc[h][e];
+#pragma unroll
+    for (int h = 0; h < NL; ++h) lv[h] = h < G ? l[h] : 0.0f;
+    float u[N / 4], ul[NL / 4];
+    rows8_sum<N>(v, u);
+    rows8_sum<NL>(lv, ul);
+    // u[k] in 16-lane group r = lane / 16 holds value 4k + r of this lane's
+    // channel chunk (lanes 8..15 of a group duplicate lanes 0..7).
+    const int r = lane / 16;
+    if ((lane & 8) == 0) {
+#pragma unroll
+      for (int k = 0; k < N / 4; ++k) {
+        const int vi = 4 * k + r;
+        red_acc[wave][0][vi / VEC][ch0 + vi % VEC] = u[k];
+      }
+      if (lane % 16 == 0) {
+#pragma unroll
+        for (int k = 0; k < NL / 4; ++k)
+          if (4 * k + r < G) red_l[wave][0][4 * k + r] = ul[k];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (lane == 0) red_m[wave][h] = m[h];
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4)
+        *reinterpret_cast<float4*>(&red_acc[wave][row][h][ch0 + e]) =
+            make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+      if (lane % LPR == 0) red_l[wave][row][h] = l[h];
+      if (lane == 0) red_m[wave][h] = m[h];
+    }
   }
   __syncthreads();
 
@@ -597,11 +669,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
       const float ww = __builtin_amdgcn_exp2f(red_m[w][h] - mm);   // 0 for idle waves
       float a0 = 0.0f, a1 = 0.0f, lw = 0.0f;
 #pragma unroll
-      for (int r = 0; r < TPL; ++r) {
-        const float2 a = *reinterpret_cast<const float2*>(&red_acc[w][r][h][c]);
+      for (int rr = 0; rr < NRW; ++rr) {
+        const float2 a = *reinterpret_cast<const float2*>(&red_acc[w][rr][h][c]);
         a0 += a.x;
         a1 += a.y;
-        lw += red_l[w][r][h];
+        lw += red_l[w][rr][h];
       }
       t0 = fmaf(ww, a0, t0);
       t1 = fmaf(ww, a1, t1);
