@@ -1,12 +1,15 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
-stats: kernel-trace statistics (calls, average/min/max duration per kernel).
-pmc:   HBM traffic per launch of one kernel from two counter runs
+stats:    kernel-trace statistics (calls, average/min/max duration per kernel).
+counters: median per-dispatch value of every counter collected for one kernel.
+pmc:      HBM traffic per launch of one kernel from two counter runs
        (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by what the
        same counter reads for a plain copy of known size in the same run.
 
 Usage:
   python -m paged_kv_cache_178_amd.rocprof_summary stats STATS_CSV --out FILE --cmd "..."
+  python -m paged_kv_cache_178_amd.rocprof_summary counters CSV [CSV ...] --kernel SUBSTR \
+      --out FILE --cmd "..."
   python -m paged_kv_cache_178_amd.rocprof_summary pmc --fetch CSV --write CSV \
       --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes N --kv-bytes N --sha SHA \
       --out FILE --cmd "..."
@@ -35,6 +38,22 @@ def stats(args) -> None:
             name = name[:107] + "..."
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                      f"{r['MaxNs']} |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def counters(args) -> None:
+    vals = {}
+    for path in args.csv:
+        for r in _rows(path):
+            if args.kernel in r.get("Kernel_Name", ""):
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no dispatches of the kernel in the counter files")
+    lines = [f"# Hardware counters: {args.title}", "", "Commands (one run per counter set):", "",
+             "```", args.cmd, "```", "", "| counter | dispatches | median per dispatch |",
+             "|---|---|---|"]
+    for name in sorted(vals):
+        lines.append(f"| `{name}` | {len(vals[name])} | {statistics.median(vals[name]):.0f} |")
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
@@ -97,6 +116,12 @@ def main(argv=None) -> None:
     a.add_argument("--out", required=True)
     a.add_argument("--cmd", required=True)
     a.add_argument("--title", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="")
     b = sub.add_parser("pmc")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -110,7 +135,7 @@ def main(argv=None) -> None:
     b.add_argument("--cmd", required=True)
     b.add_argument("--title", default="")
     args = ap.parse_args(argv)
-    (stats if args.mode == "stats" else pmc)(args)
+    {"stats": stats, "counters": counters, "pmc": pmc}[args.mode](args)
 
 
 if __name__ == "__main__":
