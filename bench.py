@@ -76,7 +76,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "batching", "prefill"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "batching", "prefill", "append"),
+                    default="decode")
     ap.add_argument("--history", type=int, default=4096)
     ap.add_argument("--pool-bytes", type=float, default=float(1 << 30),
                     help="total bytes of rotated pool copies (cold-cache measurement)")
@@ -204,6 +205,8 @@ def main(argv=None) -> int:
 
     if args.workload == "prefill":
         return run_prefill(args, dev, props)
+    if args.workload == "append":
+        return run_append(args, dev, props)
     decode = args.workload == "decode"
     inp = wl.llama_decode(args.history) if decode else wl.continuous_batching()
     kv_bytes = inp.kv_bytes()
@@ -506,6 +509,105 @@ def run_prefill(args, dev, props) -> int:
                                "sample": sample}
     else:
         rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_append(args, dev, props) -> int:
+    """Cache write of the chunked-prefill step: 4 sequences of 2048 cached
+    tokens each grow by a 512-token chunk (Llama-3.2-1B head shape, bf16); the
+    host allocator grows the tables, the kernel scatters the new K/V rows.
+    Bound by HBM: every row is read once and written once."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_178_amd import binding
+
+    num_seqs, cached, chunk, hkv, hq, d, bs = 4, 2048, 512, 8, 32, 64, 16
+    n_blocks = 2 * num_seqs * (cached + chunk) // bs
+    rng = np.random.default_rng(6)
+    alloc = binding.BlockAllocator(n_blocks, bs, num_seqs, (cached + chunk) // bs,
+                                   rng.permutation(n_blocks))
+    for s in range(num_seqs):
+        alloc.extend(s, cached + chunk)
+    table = alloc.block_table()
+    lens = alloc.context_lens()
+    new_start = np.arange(num_seqs + 1, dtype=np.int32) * chunk
+    n = num_seqs * chunk
+    g = torch.Generator().manual_seed(6)
+    k_pool = torch.randn((n_blocks, bs, hkv, d), generator=g).to(torch.bfloat16)
+    v_pool = torch.randn((n_blocks, bs, hkv, d), generator=g).to(torch.bfloat16)
+    k_new = torch.randn((n, hkv, d), generator=g).to(torch.bfloat16)
+    v_new = torch.randn((n, hkv, d), generator=g).to(torch.bfloat16)
+    row_bytes = 2 * n * hkv * d * 2          # K and V rows of the chunk
+    traffic_alg = 2 * row_bytes              # each read once, written once
+    per_copy = 2 * k_pool.numel() * 2 + row_bytes
+    copies = 1 if args.warm else max(1, math.ceil(args.pool_bytes / per_copy))
+    kp = k_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+    vp = v_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+    kn = k_new.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1)
+    vn = v_new.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1)
+    bt = torch.from_numpy(table).to(dev)
+    ln = torch.from_numpy(lens).to(dev)
+    ns = torch.from_numpy(new_start).to(dev)
+    q_dummy = torch.empty((n, hq, d), dtype=torch.bfloat16, device=dev)
+    desc = binding.make_desc(q_dummy, kp[0], bt, n_q_total=n)
+    plan = binding.np_plan(desc, lens, new_start)
+    grid, _, _ = plan.launch_shape()
+
+    def step(i: int) -> None:
+        c = i % copies
+        binding.np_paged_kv_append(desc, plan, kn[c], vn[c], bt, ln, ns, kp[c], vp[c])
+
+    log(f"[bench] append: {n} rows, {copies} rotating copies")
+    step(0)
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.append_kv(k_pool, v_pool, table, lens, new_start, k_new, v_new)
+    ok = (np.array_equal(oracle.paged._raw_bits(kp[0].cpu()), k_ref) and
+          np.array_equal(oracle.paged._raw_bits(vp[0].cpu()), v_ref))
+    if not ok:
+        print("bench.py: parity gate failed: pools differ from the oracle", file=sys.stderr)
+        return 1
+    log("[bench] parity gate passed: pools bit-exact")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    us = graph_us(step, K)
+    gbs = traffic_alg / (us * 1e-6) / 1e9
+    log(f"[bench] graph: {K} steps -> {us:.3f} us/step, {gbs:.1f} GB/s")
+    rec = {
+        "metric": "paged KV append GB/s (rows read + written, % HBM peak)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "KV cache write of a chunked-prefill step: 4 sequences x 512 new "
+                        "tokens after 2048 cached, Llama-3.2-1B head shape, 1 layer",
+            "rows": n, "bytes_read_plus_written": traffic_alg, "grid": list(grid),
+            "cache": f"{copies} rotating copies of pools and new rows",
+        },
+        "us_per_step": round(us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "paged_append_kernel"},
+        "device": props.name,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import time
+
+        times = []
+        t_end = time.perf_counter() + args.cpu_seconds
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            oracle.append_kv(k_pool, v_pool, table, lens, new_start, k_new, v_new)
+            times.append(time.perf_counter() - t0)
+        best = min(times)
+        rec["cpu_baseline"] = {"value": round(traffic_alg / best / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"full workload, best of {len(times)} runs"}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -69,7 +69,8 @@ typedef enum np_status {
   NP_ERR_UNSUPPORTED = 9,     /* valid, but no kernel is built for this shape  */
   NP_ERR_WORKSPACE_TOO_SMALL = 10,
   NP_ERR_BAD_PLAN = 11,       /* plan missing or made for another descriptor   */
-  NP_ERR_HIP = 12             /* a HIP launch reported an error                */
+  NP_ERR_HIP = 12,            /* a HIP launch reported an error                */
+  NP_ERR_POOL_EXHAUSTED = 13  /* the block allocator has too few free blocks   */
 } np_status;
 
 /* Shape and stride descriptor shared by every call. */
@@ -212,6 +213,63 @@ np_status np_paged_attention_prefill(const np_paged_desc* desc, const np_plan_t*
                                      const int32_t* context_lens, const int32_t* q_start,
                                      void* out, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/*
+ * Writing the cache: "grow the table, scatter the K/V" ("Day 20: I benchmarked
+ * the paged read before writing the kernel", section "What I learned": every
+ * step's write appends the new tokens' K/V before the read attends over them).
+ *
+ * Block allocator (host). A pool of n_blocks physical blocks of block_size
+ * slots, handed out to num_seqs sequences whose tables hold at most
+ * max_blocks_per_seq entries. Free blocks form a stack: the first
+ * allocations take free_order[0], free_order[1], ... (free_order NULL means
+ * 0, 1, 2, ...), and a released sequence's blocks are pushed back, its first
+ * block on top, so they are reused first, in that order. Deterministic: the
+ * same calls give the same tables. The allocator owns its host memory; tables
+ * and lengths are read through the accessors (valid until the next call that
+ * changes them) and copied to the device by the caller. Not thread-safe.
+ *
+ * np_alloc_extend grows sequence `seq` to `new_len` tokens (new_len >= its
+ * current length, at most max_blocks_per_seq * block_size), taking
+ * ceil(new_len / block_size) - (blocks it has) blocks off the stack and
+ * appending them to its table row. If too few blocks are free it returns
+ * NP_ERR_POOL_EXHAUSTED and changes nothing. np_alloc_release frees every
+ * block of `seq` and sets its length to 0. Unused table entries hold -1.
+ */
+typedef struct np_block_allocator np_block_allocator_t;
+
+np_status np_alloc_create(int32_t n_blocks, int32_t block_size, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, const int32_t* free_order,
+                          np_block_allocator_t** out);
+void np_alloc_destroy(np_block_allocator_t* alloc);
+np_status np_alloc_extend(np_block_allocator_t* alloc, int32_t seq, int32_t new_len);
+np_status np_alloc_release(np_block_allocator_t* alloc, int32_t seq);
+int32_t np_alloc_free_blocks(const np_block_allocator_t* alloc);
+/* [num_seqs][max_blocks_per_seq] row-major, -1 where unused. */
+const int32_t* np_alloc_block_table(const np_block_allocator_t* alloc);
+/* [num_seqs] token counts. */
+const int32_t* np_alloc_context_lens(const np_block_allocator_t* alloc);
+
+/*
+ * np_paged_kv_append -- scatter new K and V rows into the pool slots of their
+ * positions. For sequence s, rows new_start[s] .. new_start[s+1]-1 of k_new
+ * and v_new (each [n_q_total, Hkv, d], element strides new_stride[0] between
+ * rows and new_stride[1] between heads, channels contiguous, 16-byte aligned)
+ * are the tokens at positions past_s + i, past_s = context_lens[s] -
+ * (new_start[s+1] - new_start[s]): context_lens already counts them, as for
+ * prefill (append, then attend). Token t goes to slot t % block_size of
+ * physical block block_table[s][t / block_size] of k_pool and v_pool, all
+ * Hkv heads and d channels; nothing else in the pools changes. The table must
+ * already cover the new positions (np_alloc_extend). `plan` is a prefill plan
+ * made with new_start as q_start (it fixes the launch grid); desc.n_q_total is
+ * the number of new rows. Asynchronous on `stream`; never allocates. Rows of
+ * the same sequence must not be written by two overlapping calls.
+ */
+np_status np_paged_kv_append(const np_paged_desc* desc, const np_plan_t* plan,
+                             const void* k_new, const void* v_new,
+                             const int64_t new_stride[2], const int32_t* block_table,
+                             const int32_t* context_lens, const int32_t* new_start,
+                             void* k_pool, void* v_pool, void* stream);
 
 /*
  * Reference kernels for measurement (not part of the attention path).

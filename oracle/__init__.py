@@ -9,6 +9,7 @@ See :mod:`oracle.paged` for the definitions and their sources.
 """
 
 from .paged import (  # noqa: F401
+    append_kv,
     attention_rows,
     combine_splits_lse,
     gather_history,

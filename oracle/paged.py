@@ -27,6 +27,9 @@ Sources (pages by title, then section):
 * "Day 23: the real triton.jit paged-attention kernel", section "What I added
   today": ``past`` is a host-side integer; query position i of a chunk sees
   keys up to ``past + i``.
+* "Day 20: I benchmarked the paged read before writing the kernel", section
+  "What I learned": the cache write grows the table and scatters the new
+  tokens' K/V into their slots; the read then attends over them.
 
 Readings taken where the pages are silent (each is listed in the design notes):
 
@@ -250,3 +253,50 @@ def combine_splits_lse(parts: list[tuple[float, np.ndarray]]) -> np.ndarray:
     outs = np.stack([p[1] for p in parts]).astype(np.float64)
     w = np.exp(lse - lse.max())
     return (outs * w[:, None]).sum(axis=0) / w.sum()
+
+
+def _raw_bits(x) -> np.ndarray:
+    """The stored elements of a pool or of new rows as raw integers of the
+    same width (torch CPU tensor or numpy array), so that a copy can be
+    compared bit for bit whatever the element type."""
+    if hasattr(x, "detach"):
+        import torch
+
+        t = x.detach().to("cpu").contiguous()
+        width = {2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()]
+        return t.view(width).numpy().copy()
+    a = np.ascontiguousarray(x)
+    return a.view({2: np.int16, 4: np.int32, 8: np.int64}[a.itemsize]).copy()
+
+
+def append_kv(k_pool, v_pool, block_table, context_lens, new_start, k_new, v_new):
+    """Write new tokens' K/V rows into the pools.
+
+    Sequence s gets rows ``new_start[s] .. new_start[s+1] - 1`` of k_new and
+    v_new ([rows, Hkv, d]); they are its last tokens, at positions
+    ``past_s + i`` with ``past_s = context_lens[s] - n_s`` (the lengths already
+    count them: append, then attend). Token t goes to slot ``t % B`` of
+    physical block ``block_table[s, t // B]`` ("3. Paged KV-cache attention"
+    gives the addressing; "Day 20 ...", "What I learned", gives the write:
+    grow the table, scatter the K/V). Every other slot keeps its contents.
+
+    Returns (k, v): copies of the pools as raw-bit integer arrays with the
+    pools' shapes, so a GPU result can be compared bit for bit.
+    """
+    k = _raw_bits(k_pool)
+    v = _raw_bits(v_pool)
+    kn = _raw_bits(k_new)
+    vn = _raw_bits(v_new)
+    table = _i64(block_table)
+    lens = _i64(context_lens)
+    starts = _i64(new_start)
+    block_size = k.shape[1]
+    for s in range(len(lens)):
+        n = int(starts[s + 1] - starts[s])
+        past = int(lens[s]) - n
+        for i in range(n):
+            t = past + i
+            blk = int(table[s, t // block_size])
+            k[blk, t % block_size] = kn[starts[s] + i]
+            v[blk, t % block_size] = vn[starts[s] + i]
+    return k, v

@@ -21,6 +21,7 @@ STATUS_NAMES = [
     "NP_OK", "NP_ERR_NULL_PTR", "NP_ERR_BAD_DTYPE", "NP_ERR_BAD_SHAPE", "NP_ERR_BAD_STRIDE",
     "NP_ERR_MISALIGNED", "NP_ERR_BAD_GQA", "NP_ERR_BAD_CONTEXT_LEN", "NP_ERR_BAD_BLOCK_TABLE",
     "NP_ERR_UNSUPPORTED", "NP_ERR_WORKSPACE_TOO_SMALL", "NP_ERR_BAD_PLAN", "NP_ERR_HIP",
+    "NP_ERR_POOL_EXHAUSTED",
 ]
 STATUS = {name: i for i, name in enumerate(STATUS_NAMES)}
 
@@ -98,6 +99,25 @@ def _lib():
         lib.np_paged_attention_prefill.restype = ctypes.c_int
         lib.np_paged_attention_prefill.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P,
                                                    _P, _P, _P, _P, ctypes.c_size_t, _P]
+        lib.np_paged_kv_append.restype = ctypes.c_int
+        lib.np_paged_kv_append.argtypes = [ctypes.POINTER(Desc), _P, _P, _P,
+                                           ctypes.POINTER(ctypes.c_int64), _P, _P, _P, _P, _P,
+                                           _P]
+        lib.np_alloc_create.restype = ctypes.c_int
+        lib.np_alloc_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, _I32P, ctypes.POINTER(_P)]
+        lib.np_alloc_destroy.restype = None
+        lib.np_alloc_destroy.argtypes = [_P]
+        lib.np_alloc_extend.restype = ctypes.c_int
+        lib.np_alloc_extend.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
+        lib.np_alloc_release.restype = ctypes.c_int
+        lib.np_alloc_release.argtypes = [_P, ctypes.c_int32]
+        lib.np_alloc_free_blocks.restype = ctypes.c_int32
+        lib.np_alloc_free_blocks.argtypes = [_P]
+        lib.np_alloc_block_table.restype = _I32P
+        lib.np_alloc_block_table.argtypes = [_P]
+        lib.np_alloc_context_lens.restype = _I32P
+        lib.np_alloc_context_lens.argtypes = [_P]
         lib.np_probe_empty.restype = ctypes.c_int
         lib.np_probe_empty.argtypes = [_P]
         lib.np_probe_stream_read.restype = ctypes.c_int
@@ -278,6 +298,70 @@ def np_paged_attention_prefill(desc: Desc, plan: Plan, q, k_pool, v_pool, block_
 
 
 # --------------------------------------------------------- convenience layer
+
+
+def np_paged_kv_append(desc: Desc, plan: Plan, k_new, v_new, block_table, context_lens,
+                       new_start, k_pool, v_pool, new_stride=None, stream=None) -> None:
+    """Scatter rows of k_new / v_new ([rows, Hkv, d], device) into the pools.
+    `plan` is np_plan(desc, lens_host, new_start_host); new_stride defaults to
+    k_new's (row, head) element strides."""
+    if new_stride is None:
+        new_stride = (k_new.stride(0), k_new.stride(1))
+        if (v_new.stride(0), v_new.stride(1)) != tuple(new_stride):
+            raise ValueError("k_new and v_new must share their (row, head) strides")
+    st_arr = (ctypes.c_int64 * 2)(*new_stride)
+    st = _lib().np_paged_kv_append(ctypes.byref(desc), plan.handle, _ptr(k_new), _ptr(v_new),
+                                   st_arr, _ptr(block_table), _ptr(context_lens),
+                                   _ptr(new_start), _ptr(k_pool), _ptr(v_pool), _stream(stream))
+    if st:
+        raise NPError(st, "np_paged_kv_append")
+
+
+class BlockAllocator:
+    """Host block allocator (np_alloc_*): tables and lengths come back as
+    numpy copies."""
+
+    def __init__(self, n_blocks: int, block_size: int, num_seqs: int, max_blocks_per_seq: int,
+                 free_order=None):
+        import numpy as np
+
+        self.num_seqs, self.max_blocks = num_seqs, max_blocks_per_seq
+        fo_p, self._fo = _i32_host(free_order)
+        h = _P()
+        st = _lib().np_alloc_create(n_blocks, block_size, num_seqs, max_blocks_per_seq, fo_p,
+                                    ctypes.byref(h))
+        if st:
+            raise NPError(st, "np_alloc_create")
+        self.handle = h
+        self._np = np
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.np_alloc_destroy(self.handle)
+            self.handle = None
+
+    def extend(self, seq: int, new_len: int) -> None:
+        st = _lib().np_alloc_extend(self.handle, seq, new_len)
+        if st:
+            raise NPError(st, "np_alloc_extend")
+
+    def release(self, seq: int) -> None:
+        st = _lib().np_alloc_release(self.handle, seq)
+        if st:
+            raise NPError(st, "np_alloc_release")
+
+    def free_blocks(self) -> int:
+        return int(_lib().np_alloc_free_blocks(self.handle))
+
+    def block_table(self):
+        p = _lib().np_alloc_block_table(self.handle)
+        n = self.num_seqs * self.max_blocks
+        return self._np.ctypeslib.as_array(p, shape=(n,)).reshape(self.num_seqs,
+                                                                  self.max_blocks).copy()
+
+    def context_lens(self):
+        p = _lib().np_alloc_context_lens(self.handle)
+        return self._np.ctypeslib.as_array(p, shape=(self.num_seqs,)).copy()
 
 
 def workspace_for(plan: Plan, device):

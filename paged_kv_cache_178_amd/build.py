@@ -20,12 +20,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnp_paged.so")
 
-HIP_SOURCES = ["np_decode.hip", "np_prefill.hip", "np_probe.hip"]
+HIP_SOURCES = ["np_decode.hip", "np_prefill.hip", "np_append.hip", "np_probe.hip"]
 # Per-file flags. The prefill kernel masks by index with selects and never
 # relies on NaN propagation, so it is built without NaN semantics (max and min
 # lose their canonicalisation instructions).
 EXTRA_FLAGS = {"np_prefill.hip": ["-fno-honor-nans"]}
-HOST_SOURCES = ["np_host.cpp"]
+HOST_SOURCES = ["np_host.cpp", "np_alloc.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -140,6 +140,7 @@ const char* np_status_string(np_status s) {
     case NP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case NP_ERR_BAD_PLAN: return "plan missing or made for another descriptor";
     case NP_ERR_HIP: return "HIP error";
+    case NP_ERR_POOL_EXHAUSTED: return "block pool exhausted";
   }
   return "unknown status";
 }
@@ -218,6 +219,7 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     c.blocks_per_split = static_cast<int32_t>(bps);
     c.max_splits = static_cast<int32_t>(ceil_div(max_nb, bps));
     c.max_tiles = 0;
+    c.max_rows = 1;
     c.grid[0] = static_cast<uint32_t>(int64_t(c.max_splits) * c.hkv);
     c.grid[1] = static_cast<uint32_t>(c.num_seqs);
     c.grid[2] = 1;
@@ -253,10 +255,11 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     // kPrefillUnits units; a unit is one query head of the group times
     // kPrefillRowsPerWave query rows. Units are numbered head-fastest. Each
     // unit has two waves, which take alternate key tiles.
-    int64_t max_tiles = 0;
+    int64_t max_tiles = 0, max_rows = 0;
     std::vector<int64_t> tiles(c.num_seqs);
     for (int32_t s = 0; s < c.num_seqs; ++s) {
       const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
+      max_rows = std::max(max_rows, n_q);
       const int64_t units = c.group * ceil_div(n_q, kPrefillRowsPerWave);
       tiles[s] = ceil_div(units, kPrefillUnits);
       max_tiles = std::max(max_tiles, tiles[s]);
@@ -264,6 +267,7 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     c.blocks_per_split = 0;
     c.max_splits = 1;
     c.max_tiles = static_cast<int32_t>(max_tiles);
+    c.max_rows = static_cast<int32_t>(max_rows);
     c.grid[0] = static_cast<uint32_t>(max_tiles * c.hkv);
     c.grid[1] = static_cast<uint32_t>(c.num_seqs);
     c.grid[2] = 1;

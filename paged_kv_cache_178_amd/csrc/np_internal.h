@@ -31,6 +31,7 @@ struct np_plan_core {
   int32_t max_splits;      // over sequences
   // prefill
   int32_t max_tiles;       // workgroup tiles per (sequence, KV head), max over sequences
+  int32_t max_rows;        // query (or appended) rows of the longest sequence
   // launch
   uint32_t grid[3];
   uint32_t wg_size;

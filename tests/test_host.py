@@ -354,3 +354,31 @@ def test_prefill_entry_errors_before_launch():
     st = lib.np_paged_attention_prefill(ctypes.byref(d), dec.handle, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, FAKE, FAKE, None, 0, None)
     assert st == S["NP_ERR_BAD_PLAN"]
+
+
+def test_append_entry_errors_before_launch():
+    lens = np.array([600, 100], np.int32)
+    new_start = np.array([0, 64, 96], np.int32)
+    d = desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=600, n_q_total=96)
+    plan = B.np_plan(d, lens, new_start)
+    lib = B.library()
+    good = (ctypes.c_int64 * 2)(8 * 64, 64)
+
+    def call(dd=d, pl=plan, stride=good, **ptrs):
+        p = dict(kn=FAKE, vn=FAKE, bt=FAKE, lens=FAKE, ns=FAKE, k=FAKE, v=FAKE)
+        p.update(ptrs)
+        return lib.np_paged_kv_append(ctypes.byref(dd), pl.handle if pl else None, p["kn"],
+                                      p["vn"], stride, p["bt"], p["lens"], p["ns"], p["k"],
+                                      p["v"], None)
+
+    assert call(vn=0) == S["NP_ERR_NULL_PTR"]
+    assert call(ns=0) == S["NP_ERR_NULL_PTR"]
+    assert call(stride=None) == S["NP_ERR_NULL_PTR"]
+    assert call(kn=FAKE + 8) == S["NP_ERR_MISALIGNED"]
+    assert call(ns=FAKE + 2) == S["NP_ERR_MISALIGNED"]
+    assert call(stride=(ctypes.c_int64 * 2)(8 * 64, 32)) == S["NP_ERR_BAD_STRIDE"]
+    assert call(stride=(ctypes.c_int64 * 2)(7 * 64, 64)) == S["NP_ERR_BAD_STRIDE"]
+    assert call(stride=(ctypes.c_int64 * 2)(8 * 64 + 4, 64)) == S["NP_ERR_MISALIGNED"]
+    assert call(pl=None) == S["NP_ERR_BAD_PLAN"]
+    assert call(pl=B.np_plan(desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=600),
+                             lens)) == S["NP_ERR_BAD_PLAN"]      # a decode plan
