@@ -215,9 +215,10 @@ np_status np_paged_attention_prefill(const np_paged_desc* desc, const np_plan_t*
                                      void* stream);
 
 /*
- * Writing the cache: "grow the table, scatter the K/V" ("Day 20: I benchmarked
- * the paged read before writing the kernel", section "What I learned": every
- * step's write appends the new tokens' K/V before the read attends over them).
+ * Writing the cache ("Day 20: the number the Triton kernel has to beat",
+ * section "What I learned": each step's write first extends the sequence's
+ * block table, then stores the new tokens' K/V in their slots; the read then
+ * attends over them).
  *
  * Block allocator (host). A pool of n_blocks physical blocks of block_size
  * slots, handed out to num_seqs sequences whose tables hold at most

@@ -27,7 +27,7 @@ Sources (pages by title, then section):
 * "Day 23: the real triton.jit paged-attention kernel", section "What I added
   today": ``past`` is a host-side integer; query position i of a chunk sees
   keys up to ``past + i``.
-* "Day 20: I benchmarked the paged read before writing the kernel", section
+* "Day 20: the number the Triton kernel has to beat", section
   "What I learned": the cache write grows the table and scatters the new
   tokens' K/V into their slots; the read then attends over them.
 
@@ -277,8 +277,9 @@ def append_kv(k_pool, v_pool, block_table, context_lens, new_start, k_new, v_new
     ``past_s + i`` with ``past_s = context_lens[s] - n_s`` (the lengths already
     count them: append, then attend). Token t goes to slot ``t % B`` of
     physical block ``block_table[s, t // B]`` ("3. Paged KV-cache attention"
-    gives the addressing; "Day 20 ...", "What I learned", gives the write:
-    grow the table, scatter the K/V). Every other slot keeps its contents.
+    gives the addressing; "Day 20 ...", "What I learned", gives the write: the
+    table is extended first, then the new K/V are stored in their slots).
+    Every other slot keeps its contents.
 
     Returns (k, v): copies of the pools as raw-bit integer arrays with the
     pools' shapes, so a GPU result can be compared bit for bit.

@@ -1,7 +1,7 @@
-// Host block allocator for the paged KV cache: "grow the table, scatter the
-// K/V" ("Day 20: I benchmarked the paged read before writing the kernel",
-// section "What I learned") -- this file is the "grow the table" half; the
-// scatter is np_paged_kv_append.
+// Host block allocator for the paged KV cache. The cache write of "Day 20:
+// the number the Triton kernel has to beat" (section "What I learned") first
+// extends a sequence's block table, then stores the new K/V in their slots;
+// this file is the first half, np_paged_kv_append the second.
 //
 // Free blocks form a stack (the back of `free_` is the top): allocation pops,
 // release pushes a sequence's blocks back in reverse so its first block ends

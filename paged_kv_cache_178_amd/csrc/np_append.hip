@@ -1,6 +1,6 @@
-// Scatter of new K/V rows into the paged pool: the "scatter the K/V" half of
-// the cache write ("Day 20: I benchmarked the paged read before writing the
-// kernel", section "What I learned"). Token t of sequence s lives in slot
+// Scatter of new K/V rows into the paged pool: the second half of the cache
+// write ("Day 20: the number the Triton kernel has to beat", section "What I
+// learned": extend the table, then store the new K/V in their slots). Token t of sequence s lives in slot
 // t % block_size of physical block block_table[s][t / block_size] (the
 // paged layout of "3. Paged KV-cache attention" in "I Wrote the Three
 // Attention Kernels That Run LLM Inference"); the new rows of a sequence are
