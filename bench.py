@@ -86,6 +86,10 @@ def parse_args(argv=None):
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--blocks-per-split", type=int, default=0)
     ap.add_argument("--wgs-per-cu", type=int, default=0)
+    ap.add_argument("--schedule", type=int, default=0,
+                    help="decode schedule: 0 auto, 1 uniform splits, 2 stream-K")
+    ap.add_argument("--segment-cost", type=int, default=0,
+                    help="stream-K: fixed cost of a (sequence, KV head) in blocks (0: default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -224,7 +228,8 @@ def main(argv=None) -> int:
 
     opts = binding.PlanOpts(combine_mode=args.combine_mode,
                             force_blocks_per_split=args.blocks_per_split,
-                            wgs_per_cu=args.wgs_per_cu, num_cus=props.multi_processor_count)
+                            wgs_per_cu=args.wgs_per_cu, num_cus=props.multi_processor_count,
+                            schedule=args.schedule, segment_cost=args.segment_cost)
     desc = binding.make_desc(q, kbig[0], bt, out=out, scale=inp.scale)
     lens_h = inp.context_lens.numpy()
     bt_h = inp.block_table.numpy()
@@ -234,7 +239,8 @@ def main(argv=None) -> int:
     plan = binding.np_plan(desc, lens_h, None, opts)
     ws = binding.workspace_for(plan, dev)
     grid, wg, comb = plan.launch_shape()
-    log(f"[bench] plan: blocks/split {plan.blocks_per_split}, splits {plan.max_splits}, "
+    log(f"[bench] plan: schedule {plan.schedule}, blocks/split (stream-K: units per "
+        f"workgroup) {plan.blocks_per_split}, splits {plan.max_splits}, "
         f"grid {grid}, combine wgs {comb}, workspace {plan.workspace_bytes} B")
 
     def step(i: int) -> None:
@@ -403,15 +409,20 @@ def report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies) -
             "workload": "paged decode, continuous batching: 64 sequences, lengths uniform on "
                         "[128, 8192], Llama-3.2-1B head shape, 40000-block pool, 1 layer",
             "num_seqs": inp.num_seqs, "total_tokens": int(inp.context_lens.sum()),
-            "kv_bytes_per_step": kv_bytes, "blocks_per_split": plan.blocks_per_split,
-            "max_splits": plan.max_splits, "grid": list(grid),
+            "kv_bytes_per_step": kv_bytes,
+            "schedule": "stream-K" if plan.schedule == 2 else "uniform splits",
+            "blocks_per_split" if plan.schedule == 1 else "units_per_workgroup":
+                plan.blocks_per_split,
+            "max_splits" if plan.schedule == 1 else "max_pieces_per_segment": plan.max_splits,
+            "grid": list(grid),
             "cache": f"{copies} pool copy of {2 * inp.k_pool.numel() * 2 >> 20} MiB (> MALL)",
         },
         "us_per_step": round(us_per_step, 3),
         "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "paged_decode_kernel (bf16, d_pad 64, group 4, block 16)"},
+                     "kernel": ("paged_decode_sk_kernel" if plan.schedule == 2 else
+                                "paged_decode_kernel") + " (bf16, d_pad 64, group 4, block 16)"},
         "parity_max_abs_err": float(err.max()),
         "device": props.name,
     }

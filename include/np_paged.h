@@ -96,14 +96,22 @@ typedef struct np_paged_desc {
 /* Planner knobs; pass NULL for the defaults. */
 typedef struct np_plan_opts {
   int32_t num_cus;                /* compute units to fill; 0 => 256           */
-  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 1          */
-  int32_t min_blocks_per_split;   /* 0 => 4                                    */
+  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 1 (uniform
+                                     splits) or 2 (stream-K)                   */
+  int32_t min_blocks_per_split;   /* 0 => 4 (uniform); stream-K: least units
+                                     per workgroup, 0 => 8                     */
   int32_t max_blocks_per_split;   /* 0 => 1024 tokens' worth of blocks         */
   int32_t force_blocks_per_split; /* > 0: use exactly this split size          */
   int32_t combine_mode;           /* 0: the last split workgroup of each
                                      (sequence, KV head) merges the splits in
                                      the same launch; 1: a separate combine
                                      kernel does it                            */
+  int32_t schedule;               /* decode work split: 0 auto (stream-K when
+                                     num_seqs > 1 and nothing above asks for
+                                     uniform splits), 1 uniform splits, 2
+                                     stream-K                                  */
+  int32_t segment_cost;           /* stream-K: fixed cost of one (sequence, KV
+                                     head), in blocks; 0 => 4                  */
   int32_t reserved;               /* must be 0                                 */
 } np_plan_opts;
 
@@ -141,6 +149,17 @@ np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
  * split-KV partition of "2. Split-KV flash-decoding" with page-aligned,
  * never-empty splits. blocks_per_split = clamp(ceil(total_blocks * Hkv /
  * (num_cus * wgs_per_cu)), min, max), or the forced value.
+ * Decode, stream-K schedule (for batches of ragged lengths; the same
+ * partition into page-aligned pieces, cut for equal work instead of equal
+ * size): each (sequence, KV head) is a segment of ceil(L/block_size) blocks
+ * plus segment_cost virtual units; segments are laid end to end in
+ * (sequence, KV head) order, U units in all, and workgroup w of W =
+ * max(1, min(num_cus * wgs_per_cu, ceil(U / min_units), U)) takes units
+ * [w C, (w + 1) C), C = ceil(U / W). A segment's blocks inside one
+ * workgroup's range form a piece; a segment of several pieces is merged by
+ * the last piece to finish, in the same launch. The kernel recomputes the
+ * schedule from the device context_lens. At most 2048 sequences;
+ * force_blocks_per_split and combine_mode 1 select uniform splits.
  * Prefill: one workgroup per (sequence, KV head, tile of query rows).
  *
  * On success *out owns a new plan; the caller releases it with
@@ -156,13 +175,18 @@ void np_plan_destroy(np_plan_t* plan);
 size_t np_plan_workspace_bytes(const np_plan_t* plan);
 
 /* Read-only plan accessors (for tests and the benchmark). */
+/* Uniform splits: blocks per split and the most splits of a sequence.
+ * Stream-K: units per workgroup (C) and the most pieces of one segment. */
 int32_t np_plan_blocks_per_split(const np_plan_t* plan);
 int32_t np_plan_max_splits(const np_plan_t* plan);
+/* Decode schedule of the plan: 1 uniform splits, 2 stream-K (0 for prefill). */
+int32_t np_plan_schedule(const np_plan_t* plan);
 int32_t np_plan_is_prefill(const np_plan_t* plan);
 int64_t np_plan_num_work_items(const np_plan_t* plan);
-/* item[0..4] = sequence, kv head, split (or query tile), first block (or
- * first query row, relative to the sequence), end block (or end row).
- * Items are listed in launch order of the active workgroups. */
+/* item[0..4] = sequence, kv head, split (stream-K: workgroup; prefill: query
+ * tile), first block (or first query row, relative to the sequence), end
+ * block (or end row). Items are listed in launch order of the active
+ * workgroups (stream-K: by workgroup, then in the order it takes them). */
 np_status np_plan_work_item(const np_plan_t* plan, int64_t index, int32_t item[5]);
 /* grid[0..2] and the workgroup size of the main kernel; *combine_wgs is the
  * number of workgroups of the split-combine kernel (0 if no split). */

@@ -51,6 +51,7 @@ class PlanOpts(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32),
         ("min_blocks_per_split", ctypes.c_int32), ("max_blocks_per_split", ctypes.c_int32),
         ("force_blocks_per_split", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
+        ("schedule", ctypes.c_int32), ("segment_cost", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -82,7 +83,8 @@ def _lib():
         lib.np_plan_destroy.argtypes = [_P]
         lib.np_plan_workspace_bytes.restype = ctypes.c_size_t
         lib.np_plan_workspace_bytes.argtypes = [_P]
-        for name in ("np_plan_blocks_per_split", "np_plan_max_splits", "np_plan_is_prefill"):
+        for name in ("np_plan_blocks_per_split", "np_plan_max_splits", "np_plan_is_prefill",
+                     "np_plan_schedule"):
             getattr(lib, name).restype = ctypes.c_int32
             getattr(lib, name).argtypes = [_P]
         lib.np_plan_num_work_items.restype = ctypes.c_int64
@@ -205,6 +207,11 @@ class Plan:
     @property
     def max_splits(self) -> int:
         return int(_lib().np_plan_max_splits(self.handle))
+
+    @property
+    def schedule(self) -> int:
+        """1: uniform splits, 2: stream-K, 0: prefill."""
+        return int(_lib().np_plan_schedule(self.handle))
 
     @property
     def is_prefill(self) -> bool:

@@ -57,6 +57,8 @@ struct DecodeParams {
   int64_t o_s0, o_s1;
   int64_t bt_stride;
   int32_t hkv, hq, head_dim, max_blocks, bps, max_splits;
+  int32_t num_seqs;
+  int32_t sk_cost;   // stream-K: virtual units per segment
   float scale_log2;
 };
 
@@ -260,16 +262,15 @@ __device__ __forceinline__ float2 fetch2(const float* p) {
 // Latency-parallel: waves take splits round-robin, each lane owns float4
 // chunks of the G x d_pad output, and a batch of UB splits has all its loads
 // in flight before any is used; the per-wave states are merged through LDS.
-template <int DT, int D_PAD, int G>
-__device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh,
-                                             int splits) {
+template <int DT, int D_PAD, int G, typename PartOf>
+__device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh, int splits,
+                                             PartOf&& part_of) {
   constexpr int NW = kDecodeWaves;
   constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
   constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
   constexpr int UB = CPL > 1 ? 8 : 16;
   const int wave = threadIdx.x / kWaveSize;
   const int lane = threadIdx.x % kWaveSize;
-  const int64_t part_base = (int64_t(s) * p.hq + int64_t(kvh) * G) * p.max_splits;
 
   float mw[CPL], dw[CPL];
   float4 nw[CPL];
@@ -294,7 +295,7 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
         if (j < splits && chunk < NCH) {
           const int h = (chunk * 4) / D_PAD;
           const int c = (chunk * 4) % D_PAD;
-          const int64_t part = part_base + int64_t(h) * p.max_splits + j;
+          const int64_t part = part_of(j, h);
           ml[u][ci] = fetch2(p.ws_ml + 2 * part);
           a0[u][ci] = fetch2(p.ws_acc + part * D_PAD + c);
           a1[u][ci] = fetch2(p.ws_acc + part * D_PAD + c + 2);
@@ -412,81 +413,54 @@ __device__ __forceinline__ void pv_pair(const uint4& va, const uint4& vb, const 
 
 // ------------------------------------------------------------------ kernel
 
-template <int DT, int D_PAD, int G, int BS, bool FUSED>
-__global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
-    const DecodeParams p) {
-  constexpr int kElt = Elt<DT>::kBytes;
-  constexpr int VEC = 16 / kElt;          // elements per lane-load
-  constexpr int LPR = D_PAD / VEC;        // lanes per K/V row
-  constexpr int TPL = kWaveSize / LPR;    // slots per wave-load
+// Tile constants of one instantiation.
+template <int DT, int D_PAD, int BS>
+struct DecodeShape {
+  static constexpr int kElt = Elt<DT>::kBytes;
+  static constexpr int VEC = 16 / kElt;          // elements per lane-load
+  static constexpr int LPR = D_PAD / VEC;        // lanes per K/V row
+  static constexpr int TPL = kWaveSize / LPR;    // slots per wave-load
   static_assert(LPR >= 1 && LPR <= 32 && BS % TPL == 0, "unsupported tile shape");
-  constexpr int NLB = BS / TPL;           // wave-loads per block (per K or V)
+  static constexpr int NLB = BS / TPL;           // wave-loads per block (per K or V)
   static_assert(NLB % 2 == 0, "slots of a block are paired for P.V");
-  constexpr int NG = 4 / NLB > 1 ? 4 / NLB : 1;   // blocks per load group
-  constexpr int NW = kDecodeWaves;
+  static constexpr int NG = 4 / NLB > 1 ? 4 / NLB : 1;   // blocks per load group
+  static constexpr int NW = kDecodeWaves;
+};
 
-  const int kvh = blockIdx.x % p.hkv;
-  const int split = blockIdx.x / p.hkv;
-  const int s = blockIdx.y;
-  const int b0 = split * p.bps;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-  const int lane = threadIdx.x % kWaveSize;
-  const int row = lane / LPR;
-  const int ch0 = (lane % LPR) * VEC;
-  const bool chan_ok = ch0 < p.head_dim;
-  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
-
-  // This wave's blocks are b0 + wave + i * NW. It takes them in groups of NG:
-  // all K/V loads of a group are issued before any of its blocks is used, the
-  // loads of the next group are issued before this group computes, and table
-  // entries are read one group ahead of their loads.
-  // The first group's entries and this head group's q are read before the
-  // context length is known (table reads are clamped to the row, q reads to
-  // the real channels), so these reads share one memory round trip.
-  int ph[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int b = b0 + wave + i * NW;
-    ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
-  }
-  // q chunks of the G heads of this group. Padded channels load the last
-  // real chunk and are zeroed by a select, so every lane loads.
-  const int q_ch = chan_ok ? ch0 : p.head_dim - VEC;
-  uint4 qv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 t = load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + q_ch, kElt);
-    qv[h] = chan_ok ? t : make_uint4(0, 0, 0, 0);
-  }
-  const int L = p.lens[s];
-  // The table entries are needed only past the exit test below; tying them to
-  // this point keeps the compiler from moving their reads after it (which
-  // would add a second round trip before the first K/V load).
-#pragma unroll
-  for (int i = 0; i < NG; ++i) asm volatile("" ::"s"(ph[i]));
-  int nb = (L + BS - 1) / BS;
-  nb = nb < p.max_blocks ? nb : p.max_blocks;
-  int splits = (nb + p.bps - 1) / p.bps;
-  splits = splits < p.max_splits ? splits : p.max_splits;
-  if (split >= splits) return;
-  const int b1 = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
-  const int nwb = (b1 - b0 - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
-
-  // Online-softmax state. m[h] is shared by the whole wave (wave-uniform);
-  // l[h] and acc[h][.] are this lane's partial sums over the slots it saw.
+// Online-softmax state of one lane: m[h] is shared by the whole wave
+// (wave-uniform); l[h] and acc[h][.] are this lane's partial sums over the
+// slots it saw.
+template <int G, int VEC>
+struct LaneState {
   float m[G], l[G], acc[G][VEC];
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.0f;
+      for (int e = 0; e < VEC; ++e) acc[h][e] = 0.0f;
+    }
   }
+};
 
-  // Loads are unconditional inside a valid block: slots past the history are
-  // still inside the block, and padded channels read the last real chunk
-  // instead; both are masked by selects below, never by multiplication.
-  const int64_t head_off = int64_t(kvh) * p.kv_s2 + q_ch + int64_t(row) * p.kv_s1;
+// One wave's pass over its blocks b_first, b_first + NW, ... (nwb of them, may
+// be <= 0) of one (sequence, KV head): QK^T, online softmax and P.V into `st`.
+// ph holds the table entries of the first group (read by the caller, clamped
+// to the row); head_off addresses this lane's row and channel chunk of the
+// KV head inside a block.
+template <int DT, int D_PAD, int G, int BS>
+__device__ __forceinline__ void wave_accumulate(
+    const DecodeParams& p, const int32_t* bt_row, const int L, const int b_first, const int nwb,
+    const int64_t head_off, const int row, const uint4 (&qv)[G],
+    int (&ph)[DecodeShape<DT, D_PAD, BS>::NG],
+    LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st) {
+  using S = DecodeShape<DT, D_PAD, BS>;
+  constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, TPL = S::TPL, NLB = S::NLB;
+  constexpr int NG = S::NG, NW = S::NW;
+  float(&m)[G] = st.m;
+  float(&l)[G] = st.l;
+  float(&acc)[G][VEC] = st.acc;
 
   // One group of NG blocks: pass 1 computes the scores of every slot of the
   // group, the group max moves the running max once, pass 2 adds the weights
@@ -500,7 +474,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int lim = g0 + i < nwb ? L : 0;
-        const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
+        const int tok0 = (b_first + (g0 + i) * NW) * BS + row;
   #pragma unroll
         for (int j = 0; j < NLB; ++j) {
           const bool tok_ok = tok0 + j * TPL < lim;
@@ -531,7 +505,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int lim = g0 + i < nwb ? L : 0;
-        const int tok0 = (b0 + wave + (g0 + i) * NW) * BS + row;
+        const int tok0 = (b_first + (g0 + i) * NW) * BS + row;
         float w[NLB][G];
   #pragma unroll
         for (int j = 0; j < NLB; ++j)
@@ -581,7 +555,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     if (g0 + NG < nwb) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const int b = b0 + wave + (g0 + NG + i) * NW;
+        const int b = b_first + (g0 + NG + i) * NW;
         ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
       }
     }
@@ -599,8 +573,24 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     compute_group(g0 + NG, kb, vb);
   }
 
-  // ---- merge: rows of a wave share m, so their sums add directly; waves are
-  // weighted by 2^(m_wave - M). One barrier.
+}
+
+// Workgroup merge of the waves' states. Rows of a wave share m, so their sums
+// add directly; waves are weighted by 2^(m_wave - M). Then, for each output
+// pair of channels (c, c + 1) of head h of the group (c < head_dim), emit(h,
+// c, t0, t1, M, l) with the unnormalised sums. One barrier, plus one before
+// the LDS writes when the workgroup reuses the buffers (sync_before).
+template <int DT, int D_PAD, int G, int BS, typename Emit>
+__device__ __forceinline__ void wg_combine(const DecodeParams& p, const int wave, const int lane,
+                                           const int row, const int ch0,
+                                           const LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st,
+                                           const bool sync_before, Emit&& emit) {
+  using S = DecodeShape<DT, D_PAD, BS>;
+  constexpr int VEC = S::VEC, LPR = S::LPR, TPL = S::TPL, NW = S::NW;
+  const float(&m)[G] = st.m;
+  const float(&l)[G] = st.l;
+  const float(&acc)[G][VEC] = st.acc;
+  if (sync_before) __syncthreads();
   // The per-wave row sums (TPL rows) are formed in registers where the row
   // count is 8 (16-bit types, d_pad 64): partner rows are one DPP step and two
   // lane-swap steps apart, and each swap step halves the values a lane holds
@@ -656,7 +646,6 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   __syncthreads();
 
   // Two channels per thread.
-  const bool direct = splits == 1;
   for (int o = threadIdx.x; o < G * D_PAD / 2; o += NW * kWaveSize) {
     const int h = o / (D_PAD / 2);
     const int c = 2 * (o % (D_PAD / 2));
@@ -680,18 +669,89 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
       ll = fmaf(ww, lw, ll);
     }
     if (c >= p.head_dim) continue;
-    const int hg = kvh * G + h;
-    if (direct) {
-      const float r = 1.0f / ll;
-      const int64_t oi = int64_t(s) * p.o_s0 + int64_t(hg) * p.o_s1 + c;
-      store_out<DT>(p.out, oi, t0 * r);
-      store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
-    } else {
-      const int64_t part = (int64_t(s) * p.hq + hg) * p.max_splits + split;
-      publish2(p.ws_acc + part * D_PAD + c, t0, t1);
-      if (c == 0) publish2(p.ws_ml + 2 * part, mm, ll);
-    }
+    emit(h, c, t0, t1, mm, ll);
   }
+}
+
+template <int DT, int D_PAD, int G, int BS, bool FUSED>
+__global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
+    const DecodeParams p) {
+  using S = DecodeShape<DT, D_PAD, BS>;
+  constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, NG = S::NG, NW = S::NW;
+
+  const int kvh = blockIdx.x % p.hkv;
+  const int split = blockIdx.x / p.hkv;
+  const int s = blockIdx.y;
+  const int b0 = split * p.bps;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int lane = threadIdx.x % kWaveSize;
+  const int row = lane / LPR;
+  const int ch0 = (lane % LPR) * VEC;
+  const bool chan_ok = ch0 < p.head_dim;
+  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+
+  // This wave's blocks are b0 + wave + i * NW. It takes them in groups of NG:
+  // all K/V loads of a group are issued before any of its blocks is used, the
+  // loads of the next group are issued before this group computes, and table
+  // entries are read one group ahead of their loads.
+  // The first group's entries and this head group's q are read before the
+  // context length is known (table reads are clamped to the row, q reads to
+  // the real channels), so these reads share one memory round trip.
+  int ph[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int b = b0 + wave + i * NW;
+    ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
+  }
+  // q chunks of the G heads of this group. Padded channels load the last
+  // real chunk and are zeroed by a select, so every lane loads.
+  const int q_ch = chan_ok ? ch0 : p.head_dim - VEC;
+  uint4 qv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 t = load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + q_ch, kElt);
+    qv[h] = chan_ok ? t : make_uint4(0, 0, 0, 0);
+  }
+  const int L = p.lens[s];
+  // The table entries are needed only past the exit test below; tying them to
+  // this point keeps the compiler from moving their reads after it (which
+  // would add a second round trip before the first K/V load).
+#pragma unroll
+  for (int i = 0; i < NG; ++i) asm volatile("" ::"s"(ph[i]));
+  int nb = (L + BS - 1) / BS;
+  nb = nb < p.max_blocks ? nb : p.max_blocks;
+  int splits = (nb + p.bps - 1) / p.bps;
+  splits = splits < p.max_splits ? splits : p.max_splits;
+  if (split >= splits) return;
+  const int b1 = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
+  const int nwb = (b1 - b0 - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
+
+  LaneState<G, VEC> st;
+  st.reset();
+
+  // Loads are unconditional inside a valid block: slots past the history are
+  // still inside the block, and padded channels read the last real chunk
+  // instead; both are masked by selects below, never by multiplication.
+  const int64_t head_off = int64_t(kvh) * p.kv_s2 + q_ch + int64_t(row) * p.kv_s1;
+
+  wave_accumulate<DT, D_PAD, G, BS>(p, bt_row, L, b0 + wave, nwb, head_off, row, qv, ph, st);
+
+  const bool direct = splits == 1;
+  wg_combine<DT, D_PAD, G, BS>(
+      p, wave, lane, row, ch0, st, false,
+      [&](int h, int c, float t0, float t1, float mm, float ll) {
+        const int hg = kvh * G + h;
+        if (direct) {
+          const float r = 1.0f / ll;
+          const int64_t oi = int64_t(s) * p.o_s0 + int64_t(hg) * p.o_s1 + c;
+          store_out<DT>(p.out, oi, t0 * r);
+          store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
+        } else {
+          const int64_t part = (int64_t(s) * p.hq + hg) * p.max_splits + split;
+          publish2(p.ws_acc + part * D_PAD + c, t0, t1);
+          if (c == 0) publish2(p.ws_ml + 2 * part, mm, ll);
+        }
+      });
   if constexpr (FUSED) {
     if (direct) return;
     // Last-arriver merge: every thread waits until its partial stores are
@@ -710,9 +770,182 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     }
     __syncthreads();
     if (!last) return;
-    merge_splits<DT, D_PAD, G>(p, s, kvh, splits);
+    merge_splits<DT, D_PAD, G>(p, s, kvh, splits, [&](int j, int h) {
+      return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
+    });
     if (threadIdx.x == 0)
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------ stream-K schedule
+//
+// For ragged batches. Every (sequence, KV head) is a segment of nb_s blocks
+// followed by sk_cost virtual units that stand for the fixed cost of a
+// segment (its q loads, pipeline fill and drain, combine and merge). The
+// segments are laid end to end in (sequence, KV head) order, U units in all,
+// and workgroup w of the W in the launch takes units [w C, (w + 1) C) with
+// C = ceil(U / W): every workgroup gets the same amount of work whatever the
+// lengths, so no long split is left running alone at the end of the launch.
+// The blocks of a segment that fall in one workgroup's range form a piece;
+// a workgroup whose range holds only a segment's virtual units skips it. A
+// segment with one piece writes its output directly; otherwise each piece
+// publishes a partial and the last to arrive merges them, as with uniform
+// splits. A workgroup can share only its first and its last piece with other
+// workgroups, so a piece is stored in slot 2 w + side, side 0 if it starts at
+// the workgroup's first unit and 1 otherwise. The scan of the lengths runs on
+// the device from context_lens, so the schedule always matches the lengths
+// the kernel reads and the workspace bounds depend only on W.
+template <int DT, int D_PAD, int G, int BS>
+__global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kernel(
+    const DecodeParams p) {
+  using S = DecodeShape<DT, D_PAD, BS>;
+  constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, NG = S::NG, NW = S::NW;
+  __shared__ int sk_pre[kSkMaxSeqs + 1];   // units before each sequence's segments
+  __shared__ int sk_last;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int lane = threadIdx.x % kWaveSize;
+  const int row = lane / LPR;
+  const int ch0 = (lane % LPR) * VEC;
+  const bool chan_ok = ch0 < p.head_dim;
+  const int q_ch = chan_ok ? ch0 : p.head_dim - VEC;
+  const int w = blockIdx.x;
+  const int W = gridDim.x;
+
+  // Inclusive prefix sums of the per-sequence units, one wave, 64 sequences
+  // per pass.
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < p.num_seqs; base += kWaveSize) {
+      const int s = base + lane;
+      int u = 0;
+      if (s < p.num_seqs) {
+        int nb = (p.lens[s] + BS - 1) / BS;
+        nb = nb < p.max_blocks ? nb : p.max_blocks;
+        nb = nb > 0 ? nb : 0;
+        u = (nb + p.sk_cost) * p.hkv;
+      }
+#pragma unroll
+      for (int d = 1; d < kWaveSize; d <<= 1) {
+        const int t = __shfl_up(u, d);
+        if (lane >= d) u += t;
+      }
+      if (s < p.num_seqs) sk_pre[s + 1] = carry + u;
+      carry += __shfl(u, kWaveSize - 1);
+    }
+    if (lane == 0) sk_pre[0] = 0;
+  }
+  __syncthreads();
+  // Values read from LDS are uniform across the workgroup; readfirstlane
+  // tells the compiler so, which keeps the schedule in scalar registers and
+  // its branches uniform.
+  auto pre = [&](int i) { return __builtin_amdgcn_readfirstlane(sk_pre[i]); };
+  const int U = pre(p.num_seqs);
+  const int C = (U + W - 1) / W;
+  int u = w * C;
+  const int u_end = U < u + C ? U : u + C;
+  if (u >= u_end) return;
+  // The sequence whose segments hold unit u: the last s with sk_pre[s] <= u
+  // (every sequence has at least Hkv * sk_cost >= 1 units).
+  int s = 0;
+  {
+    int hi = p.num_seqs - 1;
+    while (s < hi) {
+      const int mid = (s + hi + 1) / 2;
+      if (pre(mid) <= u) s = mid;
+      else hi = mid - 1;
+    }
+  }
+
+  bool first_piece = true;
+  while (u < u_end) {
+    if (u >= pre(s + 1)) ++s;   // u never passes a segment end, so one step
+    const int L = p.lens[s];
+    int nb = (L + BS - 1) / BS;
+    nb = nb < p.max_blocks ? nb : p.max_blocks;
+    nb = nb > 0 ? nb : 0;
+    const int seg_units = nb + p.sk_cost;
+    const int seq_start = pre(s);
+    const int kvh = (u - seq_start) / seg_units;
+    const int seg_start = seq_start + kvh * seg_units;
+    const int seg_end = seg_start + seg_units;
+    // Units that make pieces: the real blocks, or the first unit of a segment
+    // without blocks (which then still writes its output).
+    const int real_end = seg_start + (nb > 0 ? nb : 1);
+    if (u >= real_end) {   // only virtual units of this segment here
+      u = seg_end < u_end ? seg_end : u_end;
+      continue;
+    }
+    const int b_lo = u - seg_start;
+    const int piece_end = u_end < real_end ? u_end : real_end;
+    const int b_hi = (piece_end - seg_start) < nb ? (piece_end - seg_start) : nb;
+    const int w_first = seg_start / C;
+    const int n_pieces = (real_end - 1) / C - w_first + 1;
+    const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+
+    int ph[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int b = b_lo + wave + i * NW;
+      ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
+    }
+    uint4 qv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 t =
+          load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + q_ch, kElt);
+      qv[h] = chan_ok ? t : make_uint4(0, 0, 0, 0);
+    }
+    const int nwb = (b_hi - b_lo - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
+    LaneState<G, VEC> st;
+    st.reset();
+    const int64_t head_off = int64_t(kvh) * p.kv_s2 + q_ch + int64_t(row) * p.kv_s1;
+    wave_accumulate<DT, D_PAD, G, BS>(p, bt_row, L, b_lo + wave, nwb, head_off, row, qv, ph,
+                                      st);
+
+    const bool direct = n_pieces == 1;
+    const int slot = 2 * w + (u == w * C ? 0 : 1);
+    wg_combine<DT, D_PAD, G, BS>(
+        p, wave, lane, row, ch0, st, !first_piece,
+        [&](int h, int c, float t0, float t1, float mm, float ll) {
+          if (direct) {
+            const float r = 1.0f / ll;
+            const int64_t oi = int64_t(s) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1 + c;
+            store_out<DT>(p.out, oi, t0 * r);
+            store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
+          } else {
+            const int64_t part = int64_t(slot) * G + h;
+            publish2(p.ws_acc + part * D_PAD + c, t0, t1);
+            if (c == 0) publish2(p.ws_ml + 2 * part, mm, ll);
+          }
+        });
+    first_piece = false;
+    if (!direct) {
+      // Last-arriver merge of the segment's pieces, with the ordering of the
+      // split kernel's: stores complete, then the ticket.
+      uint32_t* cnt = p.ws_cnt + int64_t(s * p.hkv + kvh) * kCounterStride;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sk_last = prev == uint32_t(n_pieces - 1);
+      }
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(sk_last)) {
+        // Piece j belongs to workgroup w_first + j; only the first can start
+        // inside its workgroup's range.
+        merge_splits<DT, D_PAD, G>(p, s, kvh, n_pieces, [&](int j, int h) {
+          const int wj = w_first + j;
+          const int side = (j == 0 && seg_start != wj * C) ? 1 : 0;
+          return int64_t(2 * wj + side) * G + h;
+        });
+        if (threadIdx.x == 0)
+          __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    u = seg_end < u_end ? seg_end : u_end;
   }
 }
 
@@ -727,13 +960,19 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams p
   int splits = (nb + p.bps - 1) / p.bps;
   splits = splits < p.max_splits ? splits : p.max_splits;
   if (splits <= 1) return;
-  merge_splits<DT, D_PAD, G>(p, s, kvh, splits);
+  merge_splits<DT, D_PAD, G>(p, s, kvh, splits, [&](int j, int h) {
+    return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
+  });
 }
 
 template <int DT, int D_PAD, int G>
 np_status launch_decode_t(const DecodeParams& prm, const np_plan_core& c, hipStream_t st) {
   constexpr int BS = 16;
   dim3 grid(c.grid[0], c.grid[1], c.grid[2]);
+  if (c.schedule == kScheduleStreamK) {
+    paged_decode_sk_kernel<DT, D_PAD, G, BS><<<grid, dim3(c.wg_size), 0, st>>>(prm);
+    return hipGetLastError() == hipSuccess ? NP_OK : NP_ERR_HIP;
+  }
   if (c.fused_combine)
     paged_decode_kernel<DT, D_PAD, G, BS, true><<<grid, dim3(c.wg_size), 0, st>>>(prm);
   else
@@ -828,6 +1067,8 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
   prm.max_blocks = c.max_blocks;
   prm.bps = c.blocks_per_split;
   prm.max_splits = c.max_splits;
+  prm.num_seqs = c.num_seqs;
+  prm.sk_cost = c.sk_cost;
   const float scale = desc->scale > 0.0f ? desc->scale : 1.0f / std::sqrt(float(c.head_dim));
   prm.scale_log2 = scale * kLog2e;
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -158,6 +158,73 @@ np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
   return check_host_arrays(desc, context_lens_host, q_start_host, block_table_host);
 }
 
+namespace np {
+namespace {
+
+// Stream-K decode schedule (the kernel recomputes it on the device from the
+// lengths it reads; this copy sizes the launch and lists the pieces). Each
+// (sequence, KV head) is a segment of its blocks plus sk_cost virtual units;
+// segments in (sequence, KV head) order, U units in all, W workgroups of C =
+// ceil(U / W) consecutive units. A piece is the part of a segment's blocks
+// inside one workgroup's range.
+void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
+                   std::vector<int32_t>& items) {
+  const int64_t cost = c.sk_cost;
+  std::vector<int64_t> nb(c.num_seqs);
+  int64_t U = 0;
+  for (int32_t s = 0; s < c.num_seqs; ++s) {
+    nb[s] = std::min<int64_t>(ceil_div(lens[s], c.block_size), c.max_blocks);
+    U += (nb[s] + cost) * c.hkv;
+  }
+  const int64_t num_cus = o.num_cus ? o.num_cus : 256;
+  const int64_t per_cu = o.wgs_per_cu ? o.wgs_per_cu : kSkWgsPerCu;
+  const int64_t min_units = o.min_blocks_per_split ? o.min_blocks_per_split : kSkMinUnits;
+  int64_t W = std::min(num_cus * per_cu, ceil_div(U, min_units));
+  W = std::max<int64_t>(1, std::min(W, U));
+  const int64_t C = ceil_div(U, W);
+  int64_t max_pieces = 1;
+  int64_t seg_start = 0;
+  // pieces[w] in unit order; built segment by segment, then emitted by w.
+  std::vector<std::vector<int32_t>> by_wg(W);
+  for (int32_t s = 0; s < c.num_seqs; ++s) {
+    for (int32_t kvh = 0; kvh < c.hkv; ++kvh) {
+      const int64_t real_end = seg_start + std::max<int64_t>(nb[s], 1);
+      const int64_t w_first = seg_start / C, w_last = (real_end - 1) / C;
+      max_pieces = std::max(max_pieces, w_last - w_first + 1);
+      for (int64_t w = w_first; w <= w_last; ++w) {
+        const int64_t lo = std::max(seg_start, w * C) - seg_start;
+        const int64_t hi = std::min(real_end, (w + 1) * C) - seg_start;
+        const int32_t item[5] = {s, kvh, int32_t(w), int32_t(lo),
+                                 int32_t(std::min<int64_t>(hi, nb[s]))};
+        by_wg[w].insert(by_wg[w].end(), item, item + 5);
+      }
+      seg_start += nb[s] + cost;
+    }
+  }
+  for (const auto& v : by_wg) items.insert(items.end(), v.begin(), v.end());
+  c.schedule = kScheduleStreamK;
+  c.blocks_per_split = static_cast<int32_t>(C);
+  c.max_splits = static_cast<int32_t>(max_pieces);
+  c.max_tiles = 0;
+  c.max_rows = 1;
+  c.grid[0] = static_cast<uint32_t>(W);
+  c.grid[1] = c.grid[2] = 1;
+  c.wg_size = kDecodeWaves * kWaveSize;
+  c.fused_combine = 1;
+  c.combine_wgs = 0;
+  // Counters, then two partial slots per workgroup; always present, since the
+  // device lengths decide which segments are shared.
+  auto round = [](size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; };
+  const size_t n_part = size_t(2 * W) * c.group;
+  c.ws_cnt_off = 0;
+  c.ws_ml_off = round(size_t(c.num_seqs) * c.hkv * kCounterStride * sizeof(uint32_t));
+  c.ws_acc_off = c.ws_ml_off + round(n_part * 2 * sizeof(float));
+  c.ws_bytes = c.ws_acc_off + round(n_part * c.d_pad * sizeof(float));
+}
+
+}  // namespace
+}  // namespace np
+
 np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t* q_start,
                   const np_plan_opts* opts, np_plan_t** out) {
   if (out == nullptr || lens == nullptr) return NP_ERR_NULL_PTR;
@@ -170,7 +237,12 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
   if (opts) o = *opts;
   if (o.reserved != 0 || o.num_cus < 0 || o.wgs_per_cu < 0 || o.min_blocks_per_split < 0 ||
       o.max_blocks_per_split < 0 || o.force_blocks_per_split < 0 || o.combine_mode < 0 ||
-      o.combine_mode > 1)
+      o.combine_mode > 1 || o.schedule < 0 || o.schedule > kScheduleStreamK ||
+      o.segment_cost < 0)
+    return NP_ERR_BAD_SHAPE;
+  // Stream-K replaces the split size and the separate combine.
+  if (o.schedule == kScheduleStreamK &&
+      (o.force_blocks_per_split > 0 || o.combine_mode != 0 || desc->num_seqs > kSkMaxSeqs))
     return NP_ERR_BAD_SHAPE;
   const int32_t num_cus = o.num_cus ? o.num_cus : 256;
   const int32_t wgs_per_cu = o.wgs_per_cu ? o.wgs_per_cu : 1;
@@ -195,7 +267,27 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
   c.d_pad = np_next_pow2(c.head_dim);
   c.is_prefill = q_start != nullptr;
 
+  bool stream_k = false;
   if (!c.is_prefill) {
+    const int32_t cost = o.segment_cost ? o.segment_cost : kSkDefaultCost;
+    // Units of the stream-K schedule; bounded by what the kernel can see.
+    const int64_t u_bound =
+        int64_t(c.num_seqs) * (int64_t(c.max_blocks) + cost) * c.hkv;
+    if (o.schedule == kScheduleStreamK) {
+      if (u_bound >= (int64_t(1) << 30)) {
+        delete plan;
+        return NP_ERR_BAD_SHAPE;
+      }
+      stream_k = true;
+    } else if (o.schedule == 0) {
+      stream_k = c.num_seqs > 1 && c.num_seqs <= kSkMaxSeqs && o.force_blocks_per_split == 0 &&
+                 o.combine_mode == 0 && u_bound < (int64_t(1) << 30);
+    }
+    c.sk_cost = stream_k ? cost : 0;
+  }
+  if (stream_k) {
+    plan_stream_k(c, lens, o, plan->items);
+  } else if (!c.is_prefill) {
     // Split-KV decode ("2. Split-KV flash-decoding"): page-aligned splits of a
     // uniform number of blocks, so that no split is empty and each workgroup
     // streams at most blocks_per_split blocks.
@@ -216,6 +308,7 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
       bps = std::min<int64_t>(bps, std::max(max_bps, min_bps));
     }
     bps = std::min<int64_t>(bps, std::max<int64_t>(max_nb, 1));
+    c.schedule = kScheduleUniform;
     c.blocks_per_split = static_cast<int32_t>(bps);
     c.max_splits = static_cast<int32_t>(ceil_div(max_nb, bps));
     c.max_tiles = 0;
@@ -264,6 +357,7 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
       tiles[s] = ceil_div(units, kPrefillUnits);
       max_tiles = std::max(max_tiles, tiles[s]);
     }
+    c.schedule = 0;
     c.blocks_per_split = 0;
     c.max_splits = 1;
     c.max_tiles = static_cast<int32_t>(max_tiles);
@@ -312,6 +406,10 @@ int32_t np_plan_blocks_per_split(const np_plan_t* p) {
 
 int32_t np_plan_max_splits(const np_plan_t* p) {
   return (p && p->magic == kPlanMagic) ? p->core.max_splits : -1;
+}
+
+int32_t np_plan_schedule(const np_plan_t* p) {
+  return (p && p->magic == kPlanMagic) ? p->core.schedule : -1;
 }
 
 int32_t np_plan_is_prefill(const np_plan_t* p) {

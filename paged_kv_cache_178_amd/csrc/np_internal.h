@@ -19,6 +19,12 @@ constexpr int kPrefillRowsPerWave = 64;        // query rows of one head per wav
 constexpr int kMaxGroup = 8;                   // largest Hq/Hkv with a kernel
 constexpr size_t kWsAlign = 256;
 constexpr int kCounterStride = 64;             // uint32 words between arrival counters
+constexpr int kScheduleUniform = 1;            // decode: uniform page-aligned splits
+constexpr int kScheduleStreamK = 2;            // decode: equal work per workgroup
+constexpr int kSkMaxSeqs = 2048;               // stream-K: sequences per launch
+constexpr int kSkDefaultCost = 4;              // stream-K: virtual blocks per segment
+constexpr int kSkWgsPerCu = 2;                 // stream-K: resident decode workgroups per CU
+constexpr int kSkMinUnits = 8;                 // stream-K: least units per workgroup
 
 // Sizes every launch depends on, fixed when the plan is made.
 struct np_plan_core {
@@ -27,8 +33,10 @@ struct np_plan_core {
   int32_t d_pad;           // next power of two >= head_dim
   int32_t is_prefill;
   // decode
-  int32_t blocks_per_split;
-  int32_t max_splits;      // over sequences
+  int32_t schedule;        // kScheduleUniform or kScheduleStreamK
+  int32_t blocks_per_split;  // uniform: blocks per split; stream-K: units per workgroup
+  int32_t max_splits;      // over sequences (stream-K: pieces of one segment)
+  int32_t sk_cost;         // stream-K: virtual units per (sequence, KV head)
   // prefill
   int32_t max_tiles;       // workgroup tiles per (sequence, KV head), max over sequences
   int32_t max_rows;        // query (or appended) rows of the longest sequence
@@ -39,8 +47,8 @@ struct np_plan_core {
   int32_t fused_combine;    // splits merged by the last arriving workgroup
   // workspace (bytes from the workspace base)
   size_t ws_cnt_off;       // uint32 arrival counters [num_seqs][Hkv], kCounterStride apart
-  size_t ws_ml_off;        // float2 (m, l) [num_seqs][Hq][max_splits]
-  size_t ws_acc_off;       // float [num_seqs][Hq][max_splits][d_pad]
+  size_t ws_ml_off;        // float2 (m, l) [num_seqs][Hq][max_splits] (stream-K: [2 W][G])
+  size_t ws_acc_off;       // float [num_seqs][Hq][max_splits][d_pad] (stream-K: [2 W][G][d_pad])
   size_t ws_bytes;
 };
 

@@ -44,9 +44,56 @@ def batching():
     return wl.continuous_batching()
 
 
-@pytest.mark.parametrize("combine_mode", [0, 1])
-def test_continuous_batching(batching, combine_mode):
-    _run_parity(batching, binding.PlanOpts(combine_mode=combine_mode))
+@pytest.mark.parametrize("opts", [dict(schedule=2), dict(schedule=1),
+                                  dict(schedule=1, combine_mode=1)],
+                         ids=["stream_k", "uniform_fused", "uniform_separate"])
+def test_continuous_batching(batching, opts):
+    _run_parity(batching, binding.PlanOpts(**opts))
+
+
+# Stream-K launch shapes: one workgroup for everything; one unit per
+# workgroup (every segment cut into a piece per block); a segment cost that
+# leaves workgroups holding only virtual units; the default.
+SK_SHAPES = [dict(num_cus=1, wgs_per_cu=1), dict(num_cus=300, wgs_per_cu=8, min_blocks_per_split=1,
+                                                 segment_cost=1),
+             dict(num_cus=37, wgs_per_cu=3, min_blocks_per_split=1, segment_cost=11), dict()]
+
+
+@pytest.mark.parametrize("shape", SK_SHAPES, ids=["one_wg", "unit_per_wg", "virtual_only", "auto"])
+def test_stream_k_shapes(shape):
+    inp = wl.custom(41, [1, 16, 17, 900, 4096, 33, 2000, 15], hq=32, hkv=8, d=64, dtype="bf16")
+    opts = binding.PlanOpts(schedule=2, **shape)
+    _, got = _run_parity(inp, opts)
+    base = H.gpu_decode(inp, opts=binding.PlanOpts(schedule=1))
+    diff = (got.float() - base.float()).abs().max().item()
+    assert diff <= 2 ** -7 * max(1.0, base.float().abs().max().item())
+
+
+@pytest.mark.parametrize("maker", [lambda: wl.llama_decode(4096), wl.awkward_fp16,
+                                   lambda: wl.custom(42, [3000, 5, 1200], hq=16, hkv=2, d=128,
+                                                     dtype="f32")])
+def test_stream_k_other_shapes(maker):
+    """Batch of one, head_dim 48 (fp16) and head_dim 128 (fp32) through the
+    stream-K kernel."""
+    _run_parity(maker(), binding.PlanOpts(schedule=2))
+
+
+def test_stream_k_follows_device_lengths():
+    """The stream-K kernel derives its schedule from the device lengths: a
+    plan made for other lengths (same batch) still computes the attention
+    over the lengths in device memory."""
+    inp = wl.custom(43, [4096, 700, 3000, 64], hq=32, hkv=8, d=64, dtype="bf16")
+    dev = H.to_device(inp)
+    desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], scale=inp.scale)
+    plan = binding.np_plan(desc, np.array([16, 4096, 100, 2000], np.int32), None,
+                           binding.PlanOpts(schedule=2))
+    ws = binding.workspace_for(plan, "cuda")
+    out = torch.empty_like(dev["q"])
+    binding.np_paged_attention_decode(desc, plan, dev["q"], dev["k_pool"], dev["v_pool"],
+                                      dev["block_table"], dev["context_lens"], out, ws)
+    torch.cuda.synchronize()
+    H.assert_close(out, H.oracle_out(inp), "bf16", "device lengths")
+    assert int(ws[: 256 * 4 * 8].view(torch.int32).abs().sum()) == 0
 
 
 def test_workspace_reuse_keeps_counters_zero():
@@ -56,6 +103,7 @@ def test_workspace_reuse_keeps_counters_zero():
     dev = H.to_device(inp)
     desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], scale=inp.scale)
     plan = binding.np_plan(desc, inp.context_lens)
+    assert plan.schedule == 2
     ws = binding.workspace_for(plan, "cuda")
     outs = []
     for _ in range(3):

@@ -182,7 +182,7 @@ def test_decode_plan_matches_model(seed):
     hkv = int(rng.choice([1, 2, 4, 8]))
     d = desc(num_seqs=num_seqs, hq=hkv * 4, hkv=hkv, bs=bs, n_blocks=10**6,
              max_blocks=max_blocks)
-    opts = B.PlanOpts()
+    opts = B.PlanOpts(schedule=1)
     kw = {}
     if seed % 3 == 1:
         opts.force_blocks_per_split = kw["force"] = int(rng.integers(1, 50))
@@ -193,6 +193,7 @@ def test_decode_plan_matches_model(seed):
         opts.max_blocks_per_split = kw["max_bps"] = int(rng.integers(1, 100))
     plan = B.np_plan(d, lens, None, opts)
     bps, max_splits, items = model_decode_plan(lens.tolist(), bs, hkv, **kw)
+    assert plan.schedule == 1
     assert plan.blocks_per_split == bps
     assert plan.max_splits == max_splits
     assert plan.work_items() == items
@@ -215,6 +216,100 @@ def test_decode_plan_matches_model(seed):
         assert plan.workspace_bytes == r(num_seqs * hkv * 256) + r(n_part * 8) + r(n_part * 64 * 4)
     else:
         assert plan.workspace_bytes == 0
+
+
+def model_stream_k_plan(lens, bs, hkv, max_blocks, cost=4, num_cus=256, per_cu=2,
+                        min_units=8):
+    """Brute force: intersect every workgroup's unit range with every
+    segment's block range."""
+    nbs = [min(-(-x // bs), max_blocks) for x in lens]
+    segs, start = [], 0
+    for s, nb in enumerate(nbs):
+        for kvh in range(hkv):
+            segs.append((s, kvh, nb, start))
+            start += nb + cost
+    U = start
+    W = max(1, min(num_cus * per_cu, -(-U // min_units), U))
+    C = -(-U // W)
+    items = []
+    for w in range(W):
+        lo, hi = w * C, min(U, (w + 1) * C)
+        for s, kvh, nb, st in segs:
+            a, b = max(lo, st), min(hi, st + max(nb, 1))
+            if a < b:
+                items.append((s, kvh, w, a - st, min(b - st, nb)))
+    return W, C, items
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_stream_k_plan_matches_model(seed):
+    rng = np.random.default_rng(500 + seed)
+    num_seqs = int(rng.integers(1, 70))
+    bs = int(rng.choice([1, 4, 16, 64]))
+    max_blocks = int(rng.integers(1, 400))
+    # Ragged: mostly short with a few long sequences.
+    lens = np.where(rng.random(num_seqs) < 0.2,
+                    rng.integers(1, max_blocks * bs + 1, size=num_seqs),
+                    rng.integers(1, max(2, max_blocks * bs // 8) + 1, size=num_seqs))
+    lens = np.minimum(lens, max_blocks * bs).astype(np.int32)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    d = desc(num_seqs=num_seqs, hq=hkv * 4, hkv=hkv, bs=bs, n_blocks=10**6,
+             max_blocks=max_blocks)
+    opts = B.PlanOpts(schedule=2)
+    kw = {}
+    if seed % 2:
+        opts.num_cus = kw["num_cus"] = int(rng.integers(1, 300))
+        opts.wgs_per_cu = kw["per_cu"] = int(rng.integers(1, 5))
+        opts.min_blocks_per_split = kw["min_units"] = int(rng.integers(1, 20))
+        opts.segment_cost = kw["cost"] = int(rng.integers(1, 12))
+    plan = B.np_plan(d, lens, None, opts)
+    W, C, items = model_stream_k_plan(lens.tolist(), bs, hkv, max_blocks, **kw)
+    assert plan.schedule == 2
+    assert plan.launch_shape() == ((W, 1, 1), 256, 0)
+    assert plan.blocks_per_split == C
+    assert plan.work_items() == items
+    # Every (sequence, KV head, block) exactly once; no workgroup over C units.
+    seen, per_wg, pieces = set(), {}, {}
+    for s, kvh, w, b0, b1 in items:
+        assert b1 > b0
+        for blk in range(b0, b1):
+            assert (s, kvh, blk) not in seen
+            seen.add((s, kvh, blk))
+        per_wg[w] = per_wg.get(w, 0) + (b1 - b0)
+        pieces[(s, kvh)] = pieces.get((s, kvh), 0) + 1
+    assert len(seen) == hkv * sum(-(-x // bs) for x in lens)
+    assert max(per_wg.values()) <= C
+    assert plan.max_splits == max(pieces.values())
+    # A workgroup shares at most its first and its last piece.
+    for w in range(W):
+        mine = [it for it in items if it[2] == w]
+        shared = [i for i, it in enumerate(mine) if pieces[(it[0], it[1])] > 1]
+        assert all(i in (0, len(mine) - 1) for i in shared)
+    r = lambda x: (x + 255) // 256 * 256
+    n_part = 2 * W * 4
+    assert plan.workspace_bytes == r(num_seqs * hkv * 256) + r(n_part * 8) + r(n_part * 64 * 4)
+
+
+def test_schedule_selection():
+    lens = np.array([4096, 100, 7], np.int32)
+    d = desc(num_seqs=3, hq=32, hkv=8, max_blocks=256, n_blocks=600)
+    assert B.np_plan(d, lens).schedule == 2                     # auto, batch > 1
+    assert B.np_plan(d, lens, None, B.PlanOpts(schedule=1)).schedule == 1
+    assert B.np_plan(d, lens, None, B.PlanOpts(combine_mode=1)).schedule == 1
+    assert B.np_plan(d, lens, None, B.PlanOpts(force_blocks_per_split=8)).schedule == 1
+    d1 = desc(num_seqs=1, hq=32, hkv=8, max_blocks=256, n_blocks=600)
+    one = np.array([4096], np.int32)
+    assert B.np_plan(d1, one).schedule == 1                     # auto, batch 1
+    assert B.np_plan(d1, one, None, B.PlanOpts(schedule=2)).schedule == 2
+    for bad in (B.PlanOpts(schedule=3), B.PlanOpts(schedule=-1),
+                B.PlanOpts(schedule=2, combine_mode=1),
+                B.PlanOpts(schedule=2, force_blocks_per_split=4),
+                B.PlanOpts(segment_cost=-1)):
+        with pytest.raises(B.NPError, match="BAD_SHAPE"):
+            B.np_plan(d, lens, None, bad)
+    q_start = np.array([0, 1, 2, 3], np.int32)
+    assert B.np_plan(desc(num_seqs=3, hq=32, hkv=8, max_blocks=256, n_blocks=600,
+                          n_q_total=3), lens, q_start).schedule == 0
 
 
 def test_separate_combine_mode():
@@ -243,7 +338,7 @@ def test_decode_plan_named_workloads():
     rng = np.random.default_rng(4)
     lens = rng.integers(128, 8192, size=64, endpoint=True).astype(np.int32)
     d = desc(num_seqs=64, hq=32, hkv=8, max_blocks=512, n_blocks=40000)
-    p = B.np_plan(d, lens)
+    p = B.np_plan(d, lens, None, B.PlanOpts(schedule=1))
     assert p.blocks_per_split == 64
     splits = {}
     for s, kvh, split, b0, b1 in p.work_items():
