@@ -151,14 +151,16 @@ np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
  * (num_cus * wgs_per_cu)), min, max), or the forced value.
  * Decode, stream-K schedule (for batches of ragged lengths; the same
  * partition into page-aligned pieces, cut for equal work instead of equal
- * size): each (sequence, KV head) is a segment of ceil(L/block_size) blocks
- * plus segment_cost virtual units; segments are laid end to end in
- * (sequence, KV head) order, U units in all, and workgroup w of W =
- * max(1, min(num_cus * wgs_per_cu, ceil(U / min_units), U)) takes units
- * [w C, (w + 1) C), C = ceil(U / W). A segment's blocks inside one
- * workgroup's range form a piece; a segment of several pieces is merged by
- * the last piece to finish, in the same launch. The kernel recomputes the
- * schedule from the device context_lens. At most 2048 sequences;
+ * size): a workgroup serves HW KV heads together (HW = 4, 2 or 1, the largest
+ * dividing Hkv); each (sequence, head group) is a segment of
+ * ceil(L/block_size) blocks plus segment_cost virtual units; segments are
+ * laid end to end in (sequence, head group) order, U units in all, and
+ * workgroup w of W = max(1, min(num_cus * wgs_per_cu, ceil(U / min_units),
+ * U)) takes units [w C, (w + 1) C), C = ceil(U / W). A segment's blocks
+ * inside one workgroup's range form a piece (listed as one work item per KV
+ * head of the group); a segment of several pieces is merged by the last
+ * piece to finish, in the same launch. The kernel recomputes the schedule
+ * from the device context_lens. At most 2048 sequences;
  * force_blocks_per_split and combine_mode 1 select uniform splits.
  * Prefill: one workgroup per (sequence, KV head, tile of query rows).
  *

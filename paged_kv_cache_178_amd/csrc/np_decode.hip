@@ -262,13 +262,13 @@ __device__ __forceinline__ float2 fetch2(const float* p) {
 // Latency-parallel: waves take splits round-robin, each lane owns float4
 // chunks of the G x d_pad output, and a batch of UB splits has all its loads
 // in flight before any is used; the per-wave states are merged through LDS.
-template <int DT, int D_PAD, int G, typename PartOf>
+template <int DT, int D_PAD, int G, int UB_MAX = 16, typename PartOf>
 __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh, int splits,
                                              PartOf&& part_of) {
   constexpr int NW = kDecodeWaves;
   constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
   constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
-  constexpr int UB = CPL > 1 ? 8 : 16;
+  constexpr int UB = CPL > 1 ? (UB_MAX < 8 ? UB_MAX : 8) : UB_MAX;
   const int wave = threadIdx.x / kWaveSize;
   const int lane = threadIdx.x % kWaveSize;
 
@@ -444,12 +444,13 @@ struct LaneState {
   }
 };
 
-// One wave's pass over its blocks b_first, b_first + NW, ... (nwb of them, may
-// be <= 0) of one (sequence, KV head): QK^T, online softmax and P.V into `st`.
+// One wave's pass over its blocks b_first, b_first + STRIDE, ... (nwb of them,
+// may be <= 0) of one (sequence, KV head): QK^T, online softmax and P.V into
+// `st`.
 // ph holds the table entries of the first group (read by the caller, clamped
 // to the row); head_off addresses this lane's row and channel chunk of the
 // KV head inside a block.
-template <int DT, int D_PAD, int G, int BS>
+template <int DT, int D_PAD, int G, int BS, int STRIDE = kDecodeWaves>
 __device__ __forceinline__ void wave_accumulate(
     const DecodeParams& p, const int32_t* bt_row, const int L, const int b_first, const int nwb,
     const int64_t head_off, const int row, const uint4 (&qv)[G],
@@ -457,7 +458,7 @@ __device__ __forceinline__ void wave_accumulate(
     LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st) {
   using S = DecodeShape<DT, D_PAD, BS>;
   constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, TPL = S::TPL, NLB = S::NLB;
-  constexpr int NG = S::NG, NW = S::NW;
+  constexpr int NG = S::NG;
   float(&m)[G] = st.m;
   float(&l)[G] = st.l;
   float(&acc)[G][VEC] = st.acc;
@@ -474,7 +475,7 @@ __device__ __forceinline__ void wave_accumulate(
   #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int lim = g0 + i < nwb ? L : 0;
-        const int tok0 = (b_first + (g0 + i) * NW) * BS + row;
+        const int tok0 = (b_first + (g0 + i) * STRIDE) * BS + row;
   #pragma unroll
         for (int j = 0; j < NLB; ++j) {
           const bool tok_ok = tok0 + j * TPL < lim;
@@ -505,7 +506,7 @@ __device__ __forceinline__ void wave_accumulate(
   #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int lim = g0 + i < nwb ? L : 0;
-        const int tok0 = (b_first + (g0 + i) * NW) * BS + row;
+        const int tok0 = (b_first + (g0 + i) * STRIDE) * BS + row;
         float w[NLB][G];
   #pragma unroll
         for (int j = 0; j < NLB; ++j)
@@ -555,7 +556,7 @@ __device__ __forceinline__ void wave_accumulate(
     if (g0 + NG < nwb) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const int b = b_first + (g0 + NG + i) * NW;
+        const int b = b_first + (g0 + NG + i) * STRIDE;
         ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
       }
     }
@@ -575,12 +576,14 @@ __device__ __forceinline__ void wave_accumulate(
 
 }
 
-// Workgroup merge of the waves' states. Rows of a wave share m, so their sums
-// add directly; waves are weighted by 2^(m_wave - M). Then, for each output
-// pair of channels (c, c + 1) of head h of the group (c < head_dim), emit(h,
-// c, t0, t1, M, l) with the unnormalised sums. One barrier, plus one before
-// the LDS writes when the workgroup reuses the buffers (sync_before).
-template <int DT, int D_PAD, int G, int BS, typename Emit>
+// Workgroup merge of the waves' states. The workgroup serves HW KV heads;
+// wave k holds a partial state of head k % HW. Rows of a wave share m, so
+// their sums add directly; the waves of one head are weighted by
+// 2^(m_wave - M). Then, for each output pair of channels (c, c + 1) of query
+// head h of the workgroup's HW * G (c < head_dim), emit(h, c, t0, t1, M, l)
+// with the unnormalised sums. One barrier, plus one before the LDS writes
+// when the workgroup reuses the buffers (sync_before).
+template <int DT, int D_PAD, int G, int BS, int HW, typename Emit>
 __device__ __forceinline__ void wg_combine(const DecodeParams& p, const int wave, const int lane,
                                            const int row, const int ch0,
                                            const LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st,
@@ -646,15 +649,18 @@ __device__ __forceinline__ void wg_combine(const DecodeParams& p, const int wave
   __syncthreads();
 
   // Two channels per thread.
-  for (int o = threadIdx.x; o < G * D_PAD / 2; o += NW * kWaveSize) {
-    const int h = o / (D_PAD / 2);
+  constexpr int WPH = NW / HW;   // waves per head
+  for (int o = threadIdx.x; o < HW * G * D_PAD / 2; o += NW * kWaveSize) {
+    const int hh = o / (G * D_PAD / 2);   // head of the workgroup's HW
+    const int h = (o / (D_PAD / 2)) % G;
     const int c = 2 * (o % (D_PAD / 2));
     float mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, red_m[w][h]);
+    for (int j = 0; j < WPH; ++j) mm = fmaxf(mm, red_m[hh + j * HW][h]);
     float t0 = 0.0f, t1 = 0.0f, ll = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int j = 0; j < WPH; ++j) {
+      const int w = hh + j * HW;
       const float ww = __builtin_amdgcn_exp2f(red_m[w][h] - mm);   // 0 for idle waves
       float a0 = 0.0f, a1 = 0.0f, lw = 0.0f;
 #pragma unroll
@@ -669,7 +675,7 @@ __device__ __forceinline__ void wg_combine(const DecodeParams& p, const int wave
       ll = fmaf(ww, lw, ll);
     }
     if (c >= p.head_dim) continue;
-    emit(h, c, t0, t1, mm, ll);
+    emit(hh * G + h, c, t0, t1, mm, ll);
   }
 }
 
@@ -737,7 +743,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   wave_accumulate<DT, D_PAD, G, BS>(p, bt_row, L, b0 + wave, nwb, head_off, row, qv, ph, st);
 
   const bool direct = splits == 1;
-  wg_combine<DT, D_PAD, G, BS>(
+  wg_combine<DT, D_PAD, G, BS, 1>(
       p, wave, lane, row, ch0, st, false,
       [&](int h, int c, float t0, float t1, float mm, float ll) {
         const int hg = kvh * G + h;
@@ -780,42 +786,112 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 
 // ------------------------------------------------------ stream-K schedule
 //
-// For ragged batches. Every (sequence, KV head) is a segment of nb_s blocks
-// followed by sk_cost virtual units that stand for the fixed cost of a
-// segment (its q loads, pipeline fill and drain, combine and merge). The
-// segments are laid end to end in (sequence, KV head) order, U units in all,
-// and workgroup w of the W in the launch takes units [w C, (w + 1) C) with
-// C = ceil(U / W): every workgroup gets the same amount of work whatever the
-// lengths, so no long split is left running alone at the end of the launch.
-// The blocks of a segment that fall in one workgroup's range form a piece;
-// a workgroup whose range holds only a segment's virtual units skips it. A
-// segment with one piece writes its output directly; otherwise each piece
-// publishes a partial and the last to arrive merges them, as with uniform
-// splits. A workgroup can share only its first and its last piece with other
-// workgroups, so a piece is stored in slot 2 w + side, side 0 if it starts at
-// the workgroup's first unit and 1 otherwise. The scan of the lengths runs on
-// the device from context_lens, so the schedule always matches the lengths
-// the kernel reads and the workspace bounds depend only on W.
-template <int DT, int D_PAD, int G, int BS>
-__global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kernel(
+// For ragged batches. A workgroup serves HW KV heads at once (HW = 4, 2 or 1,
+// the largest that divides Hkv): its wave k takes head k % HW, and the
+// NW / HW waves of one head take alternate blocks. So the workgroup reads HW
+// consecutive heads of every slot of a block together -- HW x 128 bytes in one
+// run for 16-bit d = 64 -- which streams from HBM markedly faster than one
+// head's row per slot spread over separate workgroups.
+//
+// Every (sequence, head group) is a segment of nb_s block units followed by
+// sk_cost virtual units that stand for the fixed cost of a segment (its q
+// loads, pipeline fill and drain, combine and merge). The segments are laid
+// end to end in (sequence, head group) order, U units in all, and workgroup w
+// of the W in the launch takes units [w C, (w + 1) C) with C = ceil(U / W):
+// every workgroup gets the same amount of work whatever the lengths, so no
+// long split is left running alone at the end of the launch. The blocks of a
+// segment that fall in one workgroup's range form a piece; a workgroup whose
+// range holds only a segment's virtual units skips it. A segment with one
+// piece writes its output directly; otherwise each piece publishes a partial
+// and the last to arrive merges them. A workgroup can share only its first
+// and its last piece with other workgroups, so a piece is stored in slot
+// 2 w + side, side 0 if it starts at the workgroup's first unit and 1
+// otherwise. The scan of the lengths runs on the device from context_lens, so
+// the schedule always matches the lengths the kernel reads and the workspace
+// bounds depend only on W.
+
+// Waves per SIMD the stream-K kernel is compiled for: three resident
+// workgroups per CU where the registers allow it without spilling (head_dim 64
+// with up to 4 heads per group, 16-bit head_dim 128 with up to 3), else no
+// constraint. The planner's default of two workgroups per CU holds for all.
+constexpr int sk_min_waves(int dt, int d_pad, int g) {
+  return (d_pad == 64 && g <= 4) || (d_pad == 128 && dt != NP_F32 && g <= 3) ? 3 : 1;
+}
+
+// Merge of the n pieces of one segment, GG query heads from head0: every
+// thread owns float4 chunks of the GG x d_pad output and folds in all pieces
+// (UB loads in flight at a time), with the split-KV page's log-sum-exp
+// weights as in merge_splits. No LDS, no barrier.
+template <int DT, int D_PAD, int GG, typename PartOf>
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int head0, int n,
+                                             PartOf&& part_of) {
+  constexpr int NCH = GG * D_PAD / 4;
+  constexpr int UB = 4;
+  for (int chunk = threadIdx.x; chunk < NCH; chunk += kDecodeWaves * kWaveSize) {
+    const int h = (chunk * 4) / D_PAD;
+    const int c = (chunk * 4) % D_PAD;
+    float mx = -INFINITY, d = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < n; j0 += UB) {
+      float2 ml[UB], a0[UB], a1[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        ml[u] = make_float2(-INFINITY, 0.0f);
+        a0[u] = a1[u] = make_float2(0.f, 0.f);
+        if (j0 + u < n) {
+          const int64_t part = part_of(j0 + u, h);
+          ml[u] = fetch2(p.ws_ml + 2 * part);
+          a0[u] = fetch2(p.ws_acc + part * D_PAD + c);
+          a1[u] = fetch2(p.ws_acc + part * D_PAD + c + 2);
+        }
+      }
+      float m_new = mx;
+#pragma unroll
+      for (int u = 0; u < UB; ++u) m_new = fmaxf(m_new, ml[u].x);
+      if (m_new == -INFINITY) continue;
+      const float a = __builtin_amdgcn_exp2f(mx - m_new);
+      d *= a;
+      acc = make_float4(acc.x * a, acc.y * a, acc.z * a, acc.w * a);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const float wu = __builtin_amdgcn_exp2f(ml[u].x - m_new);
+        d = fmaf(wu, ml[u].y, d);
+        acc.x = fmaf(wu, a0[u].x, acc.x);
+        acc.y = fmaf(wu, a0[u].y, acc.y);
+        acc.z = fmaf(wu, a1[u].x, acc.z);
+        acc.w = fmaf(wu, a1[u].y, acc.w);
+      }
+      mx = m_new;
+    }
+    const int64_t o = int64_t(s) * p.o_s0 + int64_t(head0 + h) * p.o_s1 + c;
+    const float r = 1.0f / d;
+    if (c + 0 < p.head_dim) store_out<DT>(p.out, o + 0, acc.x * r);
+    if (c + 1 < p.head_dim) store_out<DT>(p.out, o + 1, acc.y * r);
+    if (c + 2 < p.head_dim) store_out<DT>(p.out, o + 2, acc.z * r);
+    if (c + 3 < p.head_dim) store_out<DT>(p.out, o + 3, acc.w * r);
+  }
+}
+
+template <int DT, int D_PAD, int G, int BS, int HW>
+__global__ __launch_bounds__(kDecodeWaves * kWaveSize)
+__attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_decode_sk_kernel(
     const DecodeParams p) {
   using S = DecodeShape<DT, D_PAD, BS>;
   constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, NG = S::NG, NW = S::NW;
-  __shared__ int sk_pre[kSkMaxSeqs + 1];   // units before each sequence's segments
+  constexpr int WPH = NW / HW;              // waves per head
+  static_assert(NW % HW == 0, "heads per workgroup must divide the waves");
+  __shared__ int sk_pre[kSkMaxSeqs + 1];    // units before each sequence's segments
   __shared__ int sk_last;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-  const int lane = threadIdx.x % kWaveSize;
-  const int row = lane / LPR;
-  const int ch0 = (lane % LPR) * VEC;
-  const bool chan_ok = ch0 < p.head_dim;
-  const int q_ch = chan_ok ? ch0 : p.head_dim - VEC;
   const int w = blockIdx.x;
   const int W = gridDim.x;
+  const int n_hg = p.hkv / HW;              // head groups: segments per sequence
 
   // Inclusive prefix sums of the per-sequence units, one wave, 64 sequences
   // per pass.
   if (wave == 0) {
+    const int lane = threadIdx.x % kWaveSize;
     int carry = 0;
     for (int base = 0; base < p.num_seqs; base += kWaveSize) {
       const int s = base + lane;
@@ -824,7 +900,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
         int nb = (p.lens[s] + BS - 1) / BS;
         nb = nb < p.max_blocks ? nb : p.max_blocks;
         nb = nb > 0 ? nb : 0;
-        u = (nb + p.sk_cost) * p.hkv;
+        u = (nb + p.sk_cost) * n_hg;
       }
 #pragma unroll
       for (int d = 1; d < kWaveSize; d <<= 1) {
@@ -847,7 +923,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
   const int u_end = U < u + C ? U : u + C;
   if (u >= u_end) return;
   // The sequence whose segments hold unit u: the last s with sk_pre[s] <= u
-  // (every sequence has at least Hkv * sk_cost >= 1 units).
+  // (every sequence has at least n_hg * sk_cost >= 1 units).
   int s = 0;
   {
     int hi = p.num_seqs - 1;
@@ -858,6 +934,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
     }
   }
 
+  // Segments this workgroup has to merge (it held their last ticket). Only
+  // its first and its last piece can be shared, so there are at most two;
+  // the merges run after the loop, which keeps their registers out of it.
+  int n_merge = 0;
+  int mg_s[2] = {0, 0}, mg_hg[2] = {0, 0}, mg_n[2] = {0, 0}, mg_start[2] = {0, 0};
   bool first_piece = true;
   while (u < u_end) {
     if (u >= pre(s + 1)) ++s;   // u never passes a segment end, so one step
@@ -867,8 +948,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
     nb = nb > 0 ? nb : 0;
     const int seg_units = nb + p.sk_cost;
     const int seq_start = pre(s);
-    const int kvh = (u - seq_start) / seg_units;
-    const int seg_start = seq_start + kvh * seg_units;
+    const int hg = (u - seq_start) / seg_units;
+    const int seg_start = seq_start + hg * seg_units;
     const int seg_end = seg_start + seg_units;
     // Units that make pieces: the real blocks, or the first unit of a segment
     // without blocks (which then still writes its output).
@@ -877,17 +958,30 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
       u = seg_end < u_end ? seg_end : u_end;
       continue;
     }
+    // Lane coordinates are derived afresh in every piece (from an opaque copy
+    // of the thread index) so the compiler does not hoist lane-dependent
+    // addresses out of the loop and keep them live across it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid % kWaveSize;
+    const int row = lane / LPR;
+    const int ch0 = (lane % LPR) * VEC;
+    const bool chan_ok = ch0 < p.head_dim;
+    const int q_ch = chan_ok ? ch0 : p.head_dim - VEC;
     const int b_lo = u - seg_start;
     const int piece_end = u_end < real_end ? u_end : real_end;
     const int b_hi = (piece_end - seg_start) < nb ? (piece_end - seg_start) : nb;
     const int w_first = seg_start / C;
     const int n_pieces = (real_end - 1) / C - w_first + 1;
     const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+    const int kvh = hg * HW + wave % HW;      // this wave's head
+    const int phase = wave / HW;              // and its first block
+    const int b_first = b_lo + phase;
 
     int ph[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int b = b_lo + wave + i * NW;
+      const int b = b_first + i * WPH;
       ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
     }
     uint4 qv[G];
@@ -897,34 +991,35 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
           load16(p.q, int64_t(s) * p.q_s0 + int64_t(kvh * G + h) * p.q_s1 + q_ch, kElt);
       qv[h] = chan_ok ? t : make_uint4(0, 0, 0, 0);
     }
-    const int nwb = (b_hi - b_lo - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
+    const int nwb = (b_hi - b_first + WPH - 1) / WPH;   // blocks of this wave (may be <= 0)
     LaneState<G, VEC> st;
     st.reset();
     const int64_t head_off = int64_t(kvh) * p.kv_s2 + q_ch + int64_t(row) * p.kv_s1;
-    wave_accumulate<DT, D_PAD, G, BS>(p, bt_row, L, b_lo + wave, nwb, head_off, row, qv, ph,
-                                      st);
+    wave_accumulate<DT, D_PAD, G, BS, WPH>(p, bt_row, L, b_first, nwb, head_off, row, qv, ph,
+                                           st);
 
     const bool direct = n_pieces == 1;
     const int slot = 2 * w + (u == w * C ? 0 : 1);
-    wg_combine<DT, D_PAD, G, BS>(
+    const int head0 = hg * HW * G;            // first query head of the segment
+    wg_combine<DT, D_PAD, G, BS, HW>(
         p, wave, lane, row, ch0, st, !first_piece,
         [&](int h, int c, float t0, float t1, float mm, float ll) {
           if (direct) {
             const float r = 1.0f / ll;
-            const int64_t oi = int64_t(s) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1 + c;
+            const int64_t oi = int64_t(s) * p.o_s0 + int64_t(head0 + h) * p.o_s1 + c;
             store_out<DT>(p.out, oi, t0 * r);
             store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
           } else {
-            const int64_t part = int64_t(slot) * G + h;
+            const int64_t part = int64_t(slot) * (HW * G) + h;
             publish2(p.ws_acc + part * D_PAD + c, t0, t1);
             if (c == 0) publish2(p.ws_ml + 2 * part, mm, ll);
           }
         });
     first_piece = false;
     if (!direct) {
-      // Last-arriver merge of the segment's pieces, with the ordering of the
-      // split kernel's: stores complete, then the ticket.
-      uint32_t* cnt = p.ws_cnt + int64_t(s * p.hkv + kvh) * kCounterStride;
+      // Ticket, with the ordering of the split kernel's: stores complete,
+      // then the ticket.
+      uint32_t* cnt = p.ws_cnt + int64_t(s * p.hkv + hg) * kCounterStride;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -934,18 +1029,32 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_sk_kern
       }
       __syncthreads();
       if (__builtin_amdgcn_readfirstlane(sk_last)) {
-        // Piece j belongs to workgroup w_first + j; only the first can start
-        // inside its workgroup's range.
-        merge_splits<DT, D_PAD, G>(p, s, kvh, n_pieces, [&](int j, int h) {
-          const int wj = w_first + j;
-          const int side = (j == 0 && seg_start != wj * C) ? 1 : 0;
-          return int64_t(2 * wj + side) * G + h;
-        });
-        if (threadIdx.x == 0)
-          __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int i = n_merge++ > 0 ? 1 : 0;
+        mg_s[i] = s;
+        mg_hg[i] = hg;
+        mg_n[i] = n_pieces;
+        mg_start[i] = seg_start;
       }
     }
     u = seg_end < u_end ? seg_end : u_end;
+  }
+  for (int i = 0; i < n_merge; ++i) {
+    const int ms = i ? mg_s[1] : mg_s[0];
+    const int mh = i ? mg_hg[1] : mg_hg[0];
+    const int mn = i ? mg_n[1] : mg_n[0];
+    const int m0 = i ? mg_start[1] : mg_start[0];
+    const int wf = m0 / C;
+    // Piece j belongs to workgroup wf + j; only the first can start inside
+    // its workgroup's range.
+    merge_pieces<DT, D_PAD, HW * G>(p, ms, mh * HW * G, mn, [&](int j, int h) {
+      const int wj = wf + j;
+      const int side = (j == 0 && m0 != wj * C) ? 1 : 0;
+      return int64_t(2 * wj + side) * (HW * G) + h;
+    });
+    // The next call that uses the counter is ordered after this launch.
+    if (threadIdx.x == 0)
+      __hip_atomic_store(p.ws_cnt + int64_t(ms * p.hkv + mh) * kCounterStride, 0u,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -970,7 +1079,11 @@ np_status launch_decode_t(const DecodeParams& prm, const np_plan_core& c, hipStr
   constexpr int BS = 16;
   dim3 grid(c.grid[0], c.grid[1], c.grid[2]);
   if (c.schedule == kScheduleStreamK) {
-    paged_decode_sk_kernel<DT, D_PAD, G, BS><<<grid, dim3(c.wg_size), 0, st>>>(prm);
+    switch (sk_heads_per_wg(c.hkv)) {
+      case 4: paged_decode_sk_kernel<DT, D_PAD, G, BS, 4><<<grid, dim3(c.wg_size), 0, st>>>(prm); break;
+      case 2: paged_decode_sk_kernel<DT, D_PAD, G, BS, 2><<<grid, dim3(c.wg_size), 0, st>>>(prm); break;
+      default: paged_decode_sk_kernel<DT, D_PAD, G, BS, 1><<<grid, dim3(c.wg_size), 0, st>>>(prm); break;
+    }
     return hipGetLastError() == hipSuccess ? NP_OK : NP_ERR_HIP;
   }
   if (c.fused_combine)

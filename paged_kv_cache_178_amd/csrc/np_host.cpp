@@ -162,19 +162,23 @@ namespace np {
 namespace {
 
 // Stream-K decode schedule (the kernel recomputes it on the device from the
-// lengths it reads; this copy sizes the launch and lists the pieces). Each
-// (sequence, KV head) is a segment of its blocks plus sk_cost virtual units;
-// segments in (sequence, KV head) order, U units in all, W workgroups of C =
-// ceil(U / W) consecutive units. A piece is the part of a segment's blocks
-// inside one workgroup's range.
+// lengths it reads; this copy sizes the launch and lists the pieces). A
+// workgroup serves HW = sk_heads_per_wg(Hkv) KV heads at once; each
+// (sequence, head group) is a segment of its blocks plus sk_cost virtual
+// units; segments in (sequence, head group) order, U units in all, W
+// workgroups of C = ceil(U / W) consecutive units. A piece is the part of a
+// segment's blocks inside one workgroup's range; it is listed once per KV
+// head of the group.
 void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
                    std::vector<int32_t>& items) {
   const int64_t cost = c.sk_cost;
+  const int64_t hw = sk_heads_per_wg(c.hkv);
+  const int64_t n_hg = c.hkv / hw;
   std::vector<int64_t> nb(c.num_seqs);
   int64_t U = 0;
   for (int32_t s = 0; s < c.num_seqs; ++s) {
     nb[s] = std::min<int64_t>(ceil_div(lens[s], c.block_size), c.max_blocks);
-    U += (nb[s] + cost) * c.hkv;
+    U += (nb[s] + cost) * n_hg;
   }
   const int64_t num_cus = o.num_cus ? o.num_cus : 256;
   const int64_t per_cu = o.wgs_per_cu ? o.wgs_per_cu : kSkWgsPerCu;
@@ -184,19 +188,21 @@ void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
   const int64_t C = ceil_div(U, W);
   int64_t max_pieces = 1;
   int64_t seg_start = 0;
-  // pieces[w] in unit order; built segment by segment, then emitted by w.
+  // Pieces by workgroup, in unit order; built segment by segment.
   std::vector<std::vector<int32_t>> by_wg(W);
   for (int32_t s = 0; s < c.num_seqs; ++s) {
-    for (int32_t kvh = 0; kvh < c.hkv; ++kvh) {
+    for (int64_t hg = 0; hg < n_hg; ++hg) {
       const int64_t real_end = seg_start + std::max<int64_t>(nb[s], 1);
       const int64_t w_first = seg_start / C, w_last = (real_end - 1) / C;
       max_pieces = std::max(max_pieces, w_last - w_first + 1);
       for (int64_t w = w_first; w <= w_last; ++w) {
         const int64_t lo = std::max(seg_start, w * C) - seg_start;
         const int64_t hi = std::min(real_end, (w + 1) * C) - seg_start;
-        const int32_t item[5] = {s, kvh, int32_t(w), int32_t(lo),
-                                 int32_t(std::min<int64_t>(hi, nb[s]))};
-        by_wg[w].insert(by_wg[w].end(), item, item + 5);
+        for (int64_t k = 0; k < hw; ++k) {
+          const int32_t item[5] = {s, int32_t(hg * hw + k), int32_t(w), int32_t(lo),
+                                   int32_t(std::min<int64_t>(hi, nb[s]))};
+          by_wg[w].insert(by_wg[w].end(), item, item + 5);
+        }
       }
       seg_start += nb[s] + cost;
     }
@@ -212,10 +218,11 @@ void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
   c.wg_size = kDecodeWaves * kWaveSize;
   c.fused_combine = 1;
   c.combine_wgs = 0;
-  // Counters, then two partial slots per workgroup; always present, since the
-  // device lengths decide which segments are shared.
+  // Counters, then two partial slots per workgroup, each of HW * G query
+  // heads; always present, since the device lengths decide which segments
+  // are shared.
   auto round = [](size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; };
-  const size_t n_part = size_t(2 * W) * c.group;
+  const size_t n_part = size_t(2 * W) * hw * c.group;
   c.ws_cnt_off = 0;
   c.ws_ml_off = round(size_t(c.num_seqs) * c.hkv * kCounterStride * sizeof(uint32_t));
   c.ws_acc_off = c.ws_ml_off + round(n_part * 2 * sizeof(float));

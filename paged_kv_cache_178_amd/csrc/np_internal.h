@@ -26,6 +26,10 @@ constexpr int kSkDefaultCost = 4;              // stream-K: virtual blocks per s
 constexpr int kSkWgsPerCu = 2;                 // stream-K: resident decode workgroups per CU
 constexpr int kSkMinUnits = 8;                 // stream-K: least units per workgroup
 
+// Stream-K: KV heads one decode workgroup serves (the largest of 4, 2, 1 that
+// divides Hkv).
+constexpr int sk_heads_per_wg(int hkv) { return hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1; }
+
 // Sizes every launch depends on, fixed when the plan is made.
 struct np_plan_core {
   int32_t dtype, num_seqs, n_q_total, hq, hkv, head_dim, block_size, max_blocks;

@@ -220,13 +220,16 @@ def test_decode_plan_matches_model(seed):
 
 def model_stream_k_plan(lens, bs, hkv, max_blocks, cost=4, num_cus=256, per_cu=2,
                         min_units=8):
-    """Brute force: intersect every workgroup's unit range with every
-    segment's block range."""
+    """Brute force: a workgroup serves hw KV heads (the largest of 4, 2, 1
+    dividing Hkv); segments are (sequence, head group); intersect every
+    workgroup's unit range with every segment's block range. A piece is
+    listed once per head of its group."""
+    hw = 4 if hkv % 4 == 0 else 2 if hkv % 2 == 0 else 1
     nbs = [min(-(-x // bs), max_blocks) for x in lens]
     segs, start = [], 0
     for s, nb in enumerate(nbs):
-        for kvh in range(hkv):
-            segs.append((s, kvh, nb, start))
+        for hg in range(hkv // hw):
+            segs.append((s, hg, nb, start))
             start += nb + cost
     U = start
     W = max(1, min(num_cus * per_cu, -(-U // min_units), U))
@@ -234,11 +237,11 @@ def model_stream_k_plan(lens, bs, hkv, max_blocks, cost=4, num_cus=256, per_cu=2
     items = []
     for w in range(W):
         lo, hi = w * C, min(U, (w + 1) * C)
-        for s, kvh, nb, st in segs:
+        for s, hg, nb, st in segs:
             a, b = max(lo, st), min(hi, st + max(nb, 1))
             if a < b:
-                items.append((s, kvh, w, a - st, min(b - st, nb)))
-    return W, C, items
+                items += [(s, hg * hw + k, w, a - st, min(b - st, nb)) for k in range(hw)]
+    return W, C, items, hw
 
 
 @pytest.mark.parametrize("seed", range(25))
@@ -263,7 +266,7 @@ def test_stream_k_plan_matches_model(seed):
         opts.min_blocks_per_split = kw["min_units"] = int(rng.integers(1, 20))
         opts.segment_cost = kw["cost"] = int(rng.integers(1, 12))
     plan = B.np_plan(d, lens, None, opts)
-    W, C, items = model_stream_k_plan(lens.tolist(), bs, hkv, max_blocks, **kw)
+    W, C, items, hw = model_stream_k_plan(lens.tolist(), bs, hkv, max_blocks, **kw)
     assert plan.schedule == 2
     assert plan.launch_shape() == ((W, 1, 1), 256, 0)
     assert plan.blocks_per_split == C
@@ -278,15 +281,15 @@ def test_stream_k_plan_matches_model(seed):
         per_wg[w] = per_wg.get(w, 0) + (b1 - b0)
         pieces[(s, kvh)] = pieces.get((s, kvh), 0) + 1
     assert len(seen) == hkv * sum(-(-x // bs) for x in lens)
-    assert max(per_wg.values()) <= C
+    assert max(per_wg.values()) <= C * hw
     assert plan.max_splits == max(pieces.values())
     # A workgroup shares at most its first and its last piece.
     for w in range(W):
-        mine = [it for it in items if it[2] == w]
-        shared = [i for i, it in enumerate(mine) if pieces[(it[0], it[1])] > 1]
+        mine = list(dict.fromkeys((it[0], it[1] // hw) for it in items if it[2] == w))
+        shared = [i for i, (sq, hg) in enumerate(mine) if pieces[(sq, hg * hw)] > 1]
         assert all(i in (0, len(mine) - 1) for i in shared)
     r = lambda x: (x + 255) // 256 * 256
-    n_part = 2 * W * 4
+    n_part = 2 * W * hw * 4
     assert plan.workspace_bytes == r(num_seqs * hkv * 256) + r(n_part * 8) + r(n_part * 64 * 4)
 
 
