@@ -45,7 +45,9 @@ METRIC = "paged-decode KV GB/s (% HBM peak) and µs/step, Llama-3.2-1B shape @4K
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_llama_L4096_pmc.md")
+PMC_SUMMARY_BATCHING = os.path.join(ROOT, "profiles", "paged_decode_batching_64seq_pmc.md")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_decode.hip")
+HOST_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_host.cpp")
 
 
 def log(msg: str) -> None:
@@ -53,16 +55,21 @@ def log(msg: str) -> None:
 
 
 def kernel_source_sha() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the decode kernels' source and of the planner that shapes
+    their launches: a counter summary taken on other sources is stale."""
+    h = hashlib.sha256()
+    for path in (DECODE_SRC, HOST_SRC):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
+def stored_traffic(path=PMC_SUMMARY):
+    """HBM bytes per launch from a committed counter summary, if it was
     taken on the current decode kernel source; else None."""
-    if not os.path.exists(PMC_SUMMARY):
+    if not os.path.exists(path):
         return None
-    m = re.search(r"^traffic-json: (\{.*\})\s*$", open(PMC_SUMMARY).read(), re.M)
+    m = re.search(r"^traffic-json: (\{.*\})\s*$", open(path).read(), re.M)
     if not m:
         return None
     rec = json.loads(m.group(1))
@@ -247,7 +254,7 @@ def main(argv=None) -> int:
         c = i % copies
         binding.np_paged_attention_decode(desc, plan, q, kbig[c], vbig[c], bt, lens, out, ws)
 
-    if args.pmc_probe and decode:
+    if args.pmc_probe:
         for i in range(10):
             step(i)
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -255,7 +262,7 @@ def main(argv=None) -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log("[bench] pmc probe done: 10 decode steps, 3 copies of 268435456 bytes")
+        log(f"[bench] pmc probe done ({inp.name}): 10 decode steps, 3 copies of 268435456 bytes")
         return 0
 
     # ---- parity gate (on copy 0) before any timing
@@ -398,6 +405,7 @@ def main(argv=None) -> int:
 
 def report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies) -> int:
     kv_bytes = inp.kv_bytes()
+    traffic = stored_traffic(PMC_SUMMARY_BATCHING)
     gbs = kv_bytes / (us_per_step * 1e-6) / 1e9
     rec = {
         "metric": "paged-decode KV GB/s (% HBM peak), continuous batching",
@@ -420,7 +428,8 @@ def report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies) -
         "us_per_step": round(us_per_step, 3),
         "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": (None if traffic is None else traffic["traffic_bytes_per_launch"]),
                      "kernel": ("paged_decode_sk_kernel" if plan.schedule == 2 else
                                 "paged_decode_kernel") + " (bf16, d_pad 64, group 4, block 16)"},
         "parity_max_abs_err": float(err.max()),

@@ -58,22 +58,24 @@ def counters(args) -> None:
 
 
 def _per_dispatch(path, counter, substr):
+    """Counter values of the matching kernel's dispatches, in dispatch order."""
     vals = []
     for r in _rows(path):
         if r.get("Counter_Name") != counter:
             continue
         if substr in r.get("Kernel_Name", ""):
-            vals.append(float(r["Counter_Value"]))
-    return vals
+            vals.append((int(r.get("Dispatch_Id", 0)), float(r["Counter_Value"])))
+    return [v for _, v in sorted(vals)]
 
 
 def pmc(args) -> None:
     fk = _per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
     wk = _per_dispatch(args.write, "WRITE_SIZE", args.kernel)
-    # The copy kernel also serves small set-up copies: keep its n_copies
-    # largest dispatches, which are the copies of known size.
-    fc = sorted(_per_dispatch(args.fetch, "FETCH_SIZE", args.copy_kernel))[-args.n_copies:]
-    wc = sorted(_per_dispatch(args.write, "WRITE_SIZE", args.copy_kernel))[-args.n_copies:]
+    # The copy kernel also serves the set-up copies (host to device uploads,
+    # some larger): the probe's copies of known size are its last n_copies
+    # dispatches.
+    fc = _per_dispatch(args.fetch, "FETCH_SIZE", args.copy_kernel)[-args.n_copies:]
+    wc = _per_dispatch(args.write, "WRITE_SIZE", args.copy_kernel)[-args.n_copies:]
     if not (fk and wk and fc and wc):
         raise SystemExit("missing dispatches for the kernel or the copy in the counter files")
     # The copy reads and writes copy_bytes each: counter KiB -> bytes factors.
