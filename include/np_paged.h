@@ -73,6 +73,18 @@ typedef enum np_status {
   NP_ERR_POOL_EXHAUSTED = 13  /* the block allocator has too few free blocks   */
 } np_status;
 
+/*
+ * Contiguous caches. Every entry point that takes a block table accepts NULL
+ * for it: logical block j of sequence s is then physical block
+ * s * max_blocks_per_seq + j, which needs n_blocks >= num_seqs *
+ * max_blocks_per_seq (else NP_ERR_BAD_BLOCK_TABLE). With kv_stride[0] =
+ * block_size * kv_stride[1] the pools are then dense
+ * [num_seqs, max_blocks_per_seq * block_size, Hkv, d] tensors: the split-KV
+ * decode over one contiguous KV tensor of "I Wrote the Three Attention
+ * Kernels That Run LLM Inference", section "2. Split-KV flash-decoding", and
+ * its fused prefill (section "1. Fused prefill attention").
+ */
+
 /* Shape and stride descriptor shared by every call. */
 typedef struct np_paged_desc {
   int32_t dtype;              /* np_dtype of q, the pools and out              */
@@ -121,7 +133,8 @@ typedef struct np_plan_s np_plan_t;   /* opaque, host memory only */
  * np_check_paged_inputs -- validate a call without touching the GPU.
  *
  * Checks the descriptor, the device pointers (non-NULL, 16-byte aligned for
- * q/pools/out, 4-byte for int32 arrays), strides and GQA divisibility. When
+ * q/pools/out, 4-byte for int32 arrays; block_table may be NULL, see
+ * "Contiguous caches"), strides and GQA divisibility. When
  * the host copies are given it also checks 1 <= n_q_s <= context_lens[s] <=
  * max_blocks_per_seq * block_size (with q_start_host for prefill; decode has
  * one row per sequence) and that every used table entry, columns 0 ..

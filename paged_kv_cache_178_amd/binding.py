@@ -185,6 +185,36 @@ def make_desc(q, k_pool, block_table, out=None, n_q_total=None, scale=None) -> D
     return d
 
 
+def make_desc_contiguous(q, k_cache, out=None, n_q_total=None, scale=None,
+                         block_size: int = 16) -> Desc:
+    """Descriptor for dense caches k_cache/v_cache [num_seqs, capacity, Hkv, d]
+    (capacity a multiple of block_size, rows of a sequence adjacent); the
+    block table is then NULL: sequence s's block j is physical block
+    s * (capacity / block_size) + j."""
+    ns, cap, hkv, hd = (int(x) for x in k_cache.shape)
+    if cap % block_size or k_cache.stride(0) != cap * k_cache.stride(1):
+        raise ValueError("k_cache must be [num_seqs, capacity, Hkv, d] with capacity a "
+                         "multiple of block_size and sequences stored back to back")
+    d = Desc()
+    d.dtype = _dtype_code(q)
+    d.num_seqs = ns
+    d.n_q_total = int(q.shape[0]) if n_q_total is None else int(n_q_total)
+    d.num_q_heads = int(q.shape[1])
+    d.num_kv_heads = hkv
+    d.head_dim = int(q.shape[2])
+    d.block_size = block_size
+    d.max_blocks_per_seq = cap // block_size
+    d.n_blocks = ns * d.max_blocks_per_seq
+    d.q_stride[0], d.q_stride[1] = int(q.stride(0)), int(q.stride(1))
+    s1 = int(k_cache.stride(1))
+    d.kv_stride[0], d.kv_stride[1], d.kv_stride[2] = block_size * s1, s1, int(k_cache.stride(2))
+    o = q if out is None else out
+    d.out_stride[0], d.out_stride[1] = int(o.stride(0)), int(o.stride(1))
+    d.bt_stride = d.max_blocks_per_seq
+    d.scale = 0.0 if scale is None else float(scale)
+    return d
+
+
 class Plan:
     """Owns one np_plan_t."""
 

@@ -15,6 +15,7 @@
 #include <cstdint>
 
 #include "np_internal.h"
+#include "np_table.h"
 
 namespace np {
 
@@ -33,7 +34,8 @@ struct AppendParams {
   int64_t n_s0, n_s1;            // bytes between new rows, between their heads
   int64_t kv_s0, kv_s1, kv_s2;   // bytes between blocks, slots, heads of the pools
   int64_t bt_stride;             // elements
-  int32_t hkv, block_size, n_blocks, chunks_per_head;
+  int32_t bt_contig;             // 1: NULL table, contiguous layout
+  int32_t hkv, block_size, n_blocks, max_blocks, chunks_per_head;
 };
 
 __global__ __launch_bounds__(kAppendRowsPerWg * kWaveSize) void paged_append_kernel(
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kAppendRowsPerWg * kWaveSize) void paged_append_ker
   if (i >= n) return;
   const int t = p.lens[s] - n + i;   // absolute position of the row
   if (t < 0) return;                 // context_lens < new rows: nothing to write
-  const int32_t phys = p.bt[int64_t(s) * p.bt_stride + t / p.block_size];
+  const int32_t phys = table_row(p.bt, p.bt_stride, s, p.max_blocks, p.bt_contig)[t / p.block_size];
   // A table entry outside the pool (e.g. -1, never allocated) writes nothing.
   if (phys < 0 || phys >= p.n_blocks) return;
   const int slot = t % p.block_size;
@@ -81,9 +83,10 @@ extern "C" np_status np_paged_kv_append(const np_paged_desc* desc, const np_plan
                                         void* stream) {
   np_status st = check_desc(desc);
   if (st != NP_OK) return st;
-  if (!k_new || !v_new || !new_stride || !block_table || !context_lens || !new_start ||
-      !k_pool || !v_pool)
+  if (!k_new || !v_new || !new_stride || !context_lens || !new_start || !k_pool || !v_pool)
     return NP_ERR_NULL_PTR;
+  st = check_contiguous(desc, block_table);
+  if (st != NP_OK) return st;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
       reinterpret_cast<uintptr_t>(block_table) % 4 || reinterpret_cast<uintptr_t>(context_lens) % 4 ||
       reinterpret_cast<uintptr_t>(new_start) % 4)
@@ -101,7 +104,9 @@ extern "C" np_status np_paged_kv_append(const np_paged_desc* desc, const np_plan
   prm.v_new = static_cast<const char*>(v_new);
   prm.k_pool = static_cast<char*>(k_pool);
   prm.v_pool = static_cast<char*>(v_pool);
-  prm.bt = block_table;
+  // A NULL table (contiguous layout) reads a stand-in row: see np_table.h.
+  prm.bt = block_table ? block_table : context_lens;
+  prm.bt_contig = block_table == nullptr;
   prm.lens = context_lens;
   prm.new_start = new_start;
   prm.n_s0 = new_stride[0] * elt;
@@ -109,10 +114,11 @@ extern "C" np_status np_paged_kv_append(const np_paged_desc* desc, const np_plan
   prm.kv_s0 = desc->kv_stride[0] * elt;
   prm.kv_s1 = desc->kv_stride[1] * elt;
   prm.kv_s2 = desc->kv_stride[2] * elt;
-  prm.bt_stride = desc->bt_stride;
+  prm.bt_stride = block_table ? desc->bt_stride : 0;
   prm.hkv = desc->num_kv_heads;
   prm.block_size = desc->block_size;
   prm.n_blocks = desc->n_blocks;
+  prm.max_blocks = desc->max_blocks_per_seq;
   prm.chunks_per_head = static_cast<int32_t>(hd * elt / 16);   // check_desc: hd * elt % 16 == 0
   dim3 grid((c.max_rows + kAppendRowsPerWg - 1) / kAppendRowsPerWg, c.num_seqs, 1);
   paged_append_kernel<<<grid, dim3(kAppendRowsPerWg * kWaveSize), 0,

@@ -35,6 +35,7 @@
 #include <cstdint>
 
 #include "np_internal.h"
+#include "np_table.h"
 
 namespace np {
 
@@ -56,6 +57,7 @@ struct DecodeParams {
   int64_t kv_s0, kv_s1, kv_s2;
   int64_t o_s0, o_s1;
   int64_t bt_stride;
+  int32_t bt_contig;             // 1: NULL table, contiguous layout
   int32_t hkv, hq, head_dim, max_blocks, bps, max_splits;
   int32_t num_seqs;
   int32_t sk_cost;   // stream-K: virtual units per segment
@@ -447,12 +449,12 @@ struct LaneState {
 // One wave's pass over its blocks b_first, b_first + STRIDE, ... (nwb of them,
 // may be <= 0) of one (sequence, KV head): QK^T, online softmax and P.V into
 // `st`.
-// ph holds the table entries of the first group (read by the caller, clamped
-// to the row); head_off addresses this lane's row and channel chunk of the
+// ph holds the raw table entries of the first group (TableRow::raw, read by
+// the caller, clamped to the row); head_off addresses this lane's row and channel chunk of the
 // KV head inside a block.
 template <int DT, int D_PAD, int G, int BS, int STRIDE = kDecodeWaves>
 __device__ __forceinline__ void wave_accumulate(
-    const DecodeParams& p, const int32_t* bt_row, const int L, const int b_first, const int nwb,
+    const DecodeParams& p, const TableRow& bt_row, const int L, const int b_first, const int nwb,
     const int64_t head_off, const int row, const uint4 (&qv)[G],
     int (&ph)[DecodeShape<DT, D_PAD, BS>::NG],
     LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st) {
@@ -544,7 +546,8 @@ __device__ __forceinline__ void wave_accumulate(
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       if (g0 + i < nwb) {
-        const int64_t base = int64_t(ph[i]) * p.kv_s0 + head_off;
+        const int64_t base =
+            int64_t(bt_row.phys(ph[i], b_first + (g0 + i) * STRIDE)) * p.kv_s0 + head_off;
 #pragma unroll
         for (int j = 0; j < NLB; ++j) {
           kr[i][j] = load16_stream(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
@@ -557,7 +560,7 @@ __device__ __forceinline__ void wave_accumulate(
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int b = b_first + (g0 + NG + i) * STRIDE;
-        ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
+        ph[i] = bt_row.raw(b < p.max_blocks ? b : p.max_blocks - 1);
       }
     }
   };
@@ -694,7 +697,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   const int row = lane / LPR;
   const int ch0 = (lane % LPR) * VEC;
   const bool chan_ok = ch0 < p.head_dim;
-  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+  const TableRow bt_row = table_row(p.bt, p.bt_stride, s, p.max_blocks, p.bt_contig);
 
   // This wave's blocks are b0 + wave + i * NW. It takes them in groups of NG:
   // all K/V loads of a group are issued before any of its blocks is used, the
@@ -707,7 +710,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int b = b0 + wave + i * NW;
-    ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
+    ph[i] = bt_row.raw(b < p.max_blocks ? b : p.max_blocks - 1);
   }
   // q chunks of the G heads of this group. Padded channels load the last
   // real chunk and are zeroed by a select, so every lane loads.
@@ -973,7 +976,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
     const int b_hi = (piece_end - seg_start) < nb ? (piece_end - seg_start) : nb;
     const int w_first = seg_start / C;
     const int n_pieces = (real_end - 1) / C - w_first + 1;
-    const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+    const TableRow bt_row = table_row(p.bt, p.bt_stride, s, p.max_blocks, p.bt_contig);
     const int kvh = hg * HW + wave % HW;      // this wave's head
     const int phase = wave / HW;              // and its first block
     const int b_first = b_lo + phase;
@@ -982,7 +985,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int b = b_first + i * WPH;
-      ph[i] = bt_row[b < p.max_blocks ? b : p.max_blocks - 1];
+      ph[i] = bt_row.raw(b < p.max_blocks ? b : p.max_blocks - 1);
     }
     uint4 qv[G];
 #pragma unroll
@@ -1155,7 +1158,9 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
   prm.q = q;
   prm.k = k_pool;
   prm.v = v_pool;
-  prm.bt = block_table;
+  // A NULL table (contiguous layout) reads a stand-in row: see np_table.h.
+  prm.bt = block_table ? block_table : context_lens;
+  prm.bt_contig = block_table == nullptr;
   prm.lens = context_lens;
   prm.out = out;
   prm.ws_cnt = c.ws_bytes
@@ -1173,7 +1178,7 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
   prm.kv_s2 = desc->kv_stride[2];
   prm.o_s0 = desc->out_stride[0];
   prm.o_s1 = desc->out_stride[1];
-  prm.bt_stride = desc->bt_stride;
+  prm.bt_stride = block_table ? desc->bt_stride : 0;
   prm.hkv = c.hkv;
   prm.hq = c.hq;
   prm.head_dim = c.head_dim;

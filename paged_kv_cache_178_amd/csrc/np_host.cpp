@@ -65,12 +65,21 @@ np_status check_desc(const np_paged_desc* d) {
   return NP_OK;
 }
 
+np_status check_contiguous(const np_paged_desc* d, const int32_t* block_table) {
+  // Without a table, sequence s owns physical blocks s * max_blocks_per_seq ..
+  // (s + 1) * max_blocks_per_seq - 1: the pool must hold them all.
+  if (block_table == nullptr &&
+      int64_t(d->num_seqs) * d->max_blocks_per_seq > int64_t(d->n_blocks))
+    return NP_ERR_BAD_BLOCK_TABLE;
+  return NP_OK;
+}
+
 np_status check_pointers(const np_paged_desc* d, const void* q, const void* k_pool,
                          const void* v_pool, const int32_t* block_table,
                          const int32_t* context_lens, const void* out) {
-  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
-    return NP_ERR_NULL_PTR;
-  (void)d;
+  if (!q || !k_pool || !v_pool || !context_lens || !out) return NP_ERR_NULL_PTR;
+  const np_status st = check_contiguous(d, block_table);
+  if (st != NP_OK) return st;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
     return NP_ERR_MISALIGNED;
   if (!aligned(block_table, 4) || !aligned(context_lens, 4)) return NP_ERR_MISALIGNED;

@@ -68,6 +68,9 @@ namespace np {
 
 // Descriptor-level checks shared by np_check_paged_inputs and the launchers.
 np_status check_desc(const np_paged_desc* d);
+// A NULL block table (the contiguous layout) needs num_seqs * max_blocks_per_seq
+// blocks in the pool.
+np_status check_contiguous(const np_paged_desc* d, const int32_t* block_table);
 np_status check_pointers(const np_paged_desc* d, const void* q, const void* k_pool,
                          const void* v_pool, const int32_t* block_table,
                          const int32_t* context_lens, const void* out);

@@ -34,6 +34,7 @@
 #include <cstdint>
 
 #include "np_internal.h"
+#include "np_table.h"
 
 namespace np {
 
@@ -59,6 +60,7 @@ struct PrefillParams {
   int64_t kv_s0, kv_s1, kv_s2;
   int64_t o_s0, o_s1;
   int64_t bt_stride;
+  int32_t bt_contig;             // 1: NULL table, contiguous layout
   int32_t hkv, hq, group, max_blocks;
   float scale_log2;
 };
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   // lane (kp, cc) holds slots 2kp, 2kp+1 of that block, channels 8cc .. 8cc+7.
   const int kp = lane / 8;
   const int cc = lane % 8;
-  const int32_t* bt_row = p.bt + int64_t(s) * p.bt_stride;
+  const TableRow bt_row = table_row(p.bt, p.bt_stride, s, p.max_blocks, p.bt_contig);
   int nb = (L + BS - 1) / BS;
   nb = nb < p.max_blocks ? nb : p.max_blocks;
   uint4 kst[2], vst[2];
@@ -453,7 +455,9 @@ extern "C" np_status np_paged_attention_prefill(const np_paged_desc* desc,
   prm.q = q;
   prm.k = k_pool;
   prm.v = v_pool;
-  prm.bt = block_table;
+  // A NULL table (contiguous layout) reads a stand-in row: see np_table.h.
+  prm.bt = block_table ? block_table : context_lens;
+  prm.bt_contig = block_table == nullptr;
   prm.lens = context_lens;
   prm.q_start = q_start;
   prm.out = out;
@@ -464,7 +468,7 @@ extern "C" np_status np_paged_attention_prefill(const np_paged_desc* desc,
   prm.kv_s2 = desc->kv_stride[2];
   prm.o_s0 = desc->out_stride[0];
   prm.o_s1 = desc->out_stride[1];
-  prm.bt_stride = desc->bt_stride;
+  prm.bt_stride = block_table ? desc->bt_stride : 0;
   prm.hkv = c.hkv;
   prm.hq = c.hq;
   prm.group = c.group;

@@ -23,6 +23,12 @@ Recipe (fixed here, stated once):
 * K spikes (awkward workload): per sequence ``max(1, round(0.01 L))`` token
   positions drawn without replacement, K at those positions multiplied by 4 in
   float32 before rounding.
+* Contiguous caches (``identity=True``): no permutation is drawn; sequence s
+  owns blocks ``s * max_blocks .. (s + 1) * max_blocks - 1`` in order, so the
+  pool is a dense ``[num_seqs, max_blocks * B, Hkv, d]`` tensor and the table
+  is the identity (the split-KV decode and fused prefill shapes of "I Wrote
+  the Three Attention Kernels That Run LLM Inference", section "Benchmark
+  method": B = 4, H = 16, D = 64, fp16).
 """
 
 from __future__ import annotations
@@ -78,7 +84,7 @@ class PagedInputs:
 def make_paged(name: str, seed, lens, n_q, hq: int, hkv: int, d: int, block_size: int,
                dtype: str, n_blocks: int | None = None, max_blocks: int | None = None,
                spike_frac: float = 0.0, scale: float | None = None,
-               lens_rng=None) -> PagedInputs:
+               lens_rng=None, identity: bool = False) -> PagedInputs:
     """Draw one workload. ``lens`` is a list of context lengths, or a callable
     ``rng -> lens`` drawn first from the workload's generator; ``n_q`` is the
     number of query rows per sequence (an int or a list)."""
@@ -89,17 +95,21 @@ def make_paged(name: str, seed, lens, n_q, hq: int, hkv: int, d: int, block_size
     num_seqs = len(lens)
     n_q = [int(n_q)] * num_seqs if np.isscalar(n_q) else [int(x) for x in n_q]
     need = [-(-length // block_size) for length in lens]
-    if n_blocks is None:
-        n_blocks = 2 * sum(need)
     if max_blocks is None:
         max_blocks = max(need)
+    if identity:
+        n_blocks = num_seqs * max_blocks
+        table = np.arange(n_blocks, dtype=np.int32).reshape(num_seqs, max_blocks)
+    else:
+        if n_blocks is None:
+            n_blocks = 2 * sum(need)
+        perm = rng.permutation(n_blocks)
+        table = np.full((num_seqs, max_blocks), -1, dtype=np.int32)
+        cursor = 0
+        for s in range(num_seqs):
+            table[s, : need[s]] = perm[cursor: cursor + need[s]]
+            cursor += need[s]
     assert sum(need) <= n_blocks and max(need) <= max_blocks
-    perm = rng.permutation(n_blocks)
-    table = np.full((num_seqs, max_blocks), -1, dtype=np.int32)
-    cursor = 0
-    for s in range(num_seqs):
-        table[s, : need[s]] = perm[cursor: cursor + need[s]]
-        cursor += need[s]
     n_q_total = sum(n_q)
     q = rng.standard_normal((n_q_total, hq, d), dtype=np.float32)
     k = rng.standard_normal((n_blocks, block_size, hkv, d), dtype=np.float32)
@@ -168,9 +178,34 @@ def chunked_prefill(seed: int = 5, num_seqs: int = 4, cached: int = 2048,
                       32, 8, 64, 16, "bf16")
 
 
+SPLITKV_CONTEXTS = (1024, 2048, 4096, 8192, 16384)
+SPLITKV_SPLITS = (1, 8, 16, 32, 64, 128)
+
+
+def splitkv_decode(n_ctx: int, seed: int = 6) -> PagedInputs:
+    """Contiguous-cache decode sweep shape: 4 sequences of n_ctx tokens, Hq =
+    Hkv = 16, d = 64, fp16, one query row each."""
+    return make_paged(f"splitkv_N{n_ctx}", seed, [n_ctx] * 4, 1, 16, 16, 64, 16, "f16",
+                      identity=True)
+
+
+def fused_prefill(n_ctx: int, seed: int = 7, num_seqs: int = 4) -> PagedInputs:
+    """Contiguous-cache prefill of a whole prompt: num_seqs sequences of n_ctx
+    tokens, all of them queries (past = 0), Hq = Hkv = 16, d = 64, fp16."""
+    return make_paged(f"fused_prefill_N{n_ctx}", seed, [n_ctx] * num_seqs, n_ctx, 16, 16, 64,
+                      16, "f16", identity=True)
+
+
+def dense_view(pool: torch.Tensor, num_seqs: int) -> torch.Tensor:
+    """The dense [num_seqs, capacity, Hkv, d] view of an identity-table pool."""
+    nb, bs, hkv, d = pool.shape
+    return pool.view(num_seqs, (nb // num_seqs) * bs, hkv, d)
+
+
 def custom(seed: int, lens, n_q=1, hq=8, hkv=2, d=64, block_size=16, dtype="bf16",
-           n_blocks=None, max_blocks=None, spike_frac=0.0, scale=None) -> PagedInputs:
+           n_blocks=None, max_blocks=None, spike_frac=0.0, scale=None,
+           identity=False) -> PagedInputs:
     """Any other shape, same recipe (used by edge-case tests)."""
     return make_paged(f"custom_s{seed}", seed, lens, n_q, hq, hkv, d, block_size, dtype,
                       n_blocks=n_blocks, max_blocks=max_blocks, spike_frac=spike_frac,
-                      scale=scale)
+                      scale=scale, identity=identity)

@@ -89,6 +89,11 @@ def test_check_accepts_valid():
 def test_check_errors():
     assert check(desc(), ptrs={"q": 0}) == S["NP_ERR_NULL_PTR"]
     assert check(desc(), ptrs={"out": 0}) == S["NP_ERR_NULL_PTR"]
+    # A NULL table selects the contiguous layout: the pool must then hold
+    # num_seqs * max_blocks_per_seq blocks (desc(): 2 * 8 <= 64).
+    assert check(desc(), ptrs={"bt": 0}) == S["NP_OK"]
+    assert check(desc(n_blocks=15), ptrs={"bt": 0}) == S["NP_ERR_BAD_BLOCK_TABLE"]
+    assert check(desc(n_blocks=16), ptrs={"bt": 0}) == S["NP_OK"]
     assert check(desc(), ptrs={"k": FAKE + 8}) == S["NP_ERR_MISALIGNED"]
     assert check(desc(), ptrs={"lens": FAKE + 2}) == S["NP_ERR_MISALIGNED"]
     assert check(desc(dtype=7)) == S["NP_ERR_BAD_DTYPE"]
@@ -421,6 +426,8 @@ def test_decode_entry_errors_before_launch():
     assert call_decode(d, plan, ws=FAKE, ws_bytes=plan.workspace_bytes - 1) == \
         S["NP_ERR_WORKSPACE_TOO_SMALL"]
     assert call_decode(d, plan, ptrs={"v": 0}) == S["NP_ERR_NULL_PTR"]
+    small = desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=511)
+    assert call_decode(small, plan, ptrs={"bt": 0}) == S["NP_ERR_BAD_BLOCK_TABLE"]
     d32 = desc(num_seqs=2, hq=32, hkv=8, bs=32, max_blocks=128, n_blocks=600)
     assert call_decode(d32, B.np_plan(d32, lens)) == S["NP_ERR_UNSUPPORTED"]
     d16 = desc(num_seqs=2, hq=32, hkv=2, max_blocks=256, n_blocks=600)   # group 16
@@ -472,6 +479,9 @@ def test_append_entry_errors_before_launch():
     assert call(vn=0) == S["NP_ERR_NULL_PTR"]
     assert call(ns=0) == S["NP_ERR_NULL_PTR"]
     assert call(stride=None) == S["NP_ERR_NULL_PTR"]
+    # A NULL table (contiguous layout) needs num_seqs * max_blocks = 512 blocks.
+    small = desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=511, n_q_total=96)
+    assert call(dd=small, bt=0) == S["NP_ERR_BAD_BLOCK_TABLE"]
     assert call(kn=FAKE + 8) == S["NP_ERR_MISALIGNED"]
     assert call(ns=FAKE + 2) == S["NP_ERR_MISALIGNED"]
     assert call(stride=(ctypes.c_int64 * 2)(8 * 64, 32)) == S["NP_ERR_BAD_STRIDE"]
