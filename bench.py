@@ -83,7 +83,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "batching", "prefill", "append"),
+    ap.add_argument("--workload", choices=("decode", "batching", "prefill", "append", "splitkv",
+                                           "fused-prefill"),
                     default="decode")
     ap.add_argument("--history", type=int, default=4096)
     ap.add_argument("--pool-bytes", type=float, default=float(1 << 30),
@@ -218,6 +219,10 @@ def main(argv=None) -> int:
         return run_prefill(args, dev, props)
     if args.workload == "append":
         return run_append(args, dev, props)
+    if args.workload == "splitkv":
+        return run_splitkv(args, dev, props)
+    if args.workload == "fused-prefill":
+        return run_fused_prefill(args, dev, props)
     decode = args.workload == "decode"
     inp = wl.llama_decode(args.history) if decode else wl.continuous_batching()
     kv_bytes = inp.kv_bytes()
@@ -529,6 +534,220 @@ def run_prefill(args, dev, props) -> int:
                                "sample": sample}
     else:
         rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_splitkv(args, dev, props) -> int:
+    """Split-KV decode over contiguous caches (NULL block table): the
+    num_splits sweep of the contiguous-cache benchmark (B = 4, H = 16, D = 64,
+    fp16, N from 1K to 16K, num_splits 1 .. 128 as page-aligned blocks per
+    split), next to the planner's default plan."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_178_amd import binding
+    from paged_kv_cache_178_amd import workloads as wl
+
+    K = args.steps
+    sweep, default, errs = [], {}, []
+    cpu_inp = None
+    for n_ctx in wl.SPLITKV_CONTEXTS:
+        inp = wl.splitkv_decode(n_ctx)
+        if cpu_inp is None:
+            cpu_inp = inp
+        ns = inp.num_seqs
+        q = inp.q.to(dev)
+        lens = inp.context_lens.to(dev)
+        lens_h = inp.context_lens.numpy()
+        cache_bytes = 2 * inp.k_pool.numel() * inp.k_pool.element_size()
+        copies = max(1, math.ceil(args.pool_bytes / cache_bytes))
+        kbig = inp.k_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+        vbig = inp.v_pool.to(dev).unsqueeze(0).repeat(copies, 1, 1, 1, 1)
+        kd = [wl.dense_view(kbig[c], ns) for c in range(copies)]
+        vd = [wl.dense_view(vbig[c], ns) for c in range(copies)]
+        out = torch.empty_like(q)
+        desc = binding.make_desc_contiguous(q, kd[0], out=out, scale=inp.scale)
+        st = binding.np_check_paged_inputs(desc, q, kd[0], vd[0], None, lens, out, None, lens_h)
+        if st:
+            raise binding.NPError(st, "np_check_paged_inputs")
+        nb = n_ctx // 16
+        plans = [("default", binding.np_plan(desc, lens_h, None,
+                                             binding.PlanOpts(num_cus=props.multi_processor_count)))]
+        for sp in wl.SPLITKV_SPLITS:
+            bps = max(1, -(-nb // sp))
+            plans.append((sp, binding.np_plan(desc, lens_h, None,
+                                              binding.PlanOpts(force_blocks_per_split=bps))))
+        ref = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                     inp.context_lens, scale=inp.scale)
+        for name, plan in plans:
+            ws = binding.workspace_for(plan, dev)
+
+            def step(i, plan=plan, ws=ws):
+                c = i % copies
+                binding.np_paged_attention_decode(desc, plan, q, kd[c], vd[c], None, lens, out,
+                                                  ws)
+
+            step(0)
+            torch.cuda.synchronize()
+            err = np.abs(out.to("cpu", torch.float64).numpy() - ref)
+            if not (err <= 1e-2 + 1e-2 * np.abs(ref)).all():
+                print(f"bench.py: parity gate failed at N={n_ctx}, plan {name}: max abs err "
+                      f"{err.max():.3e}", file=sys.stderr)
+                return 1
+            errs.append(float(err.max()))
+            for i in range(args.warmup):
+                step(i)
+            us = graph_us(step, K)
+            gbs = inp.kv_bytes() / (us * 1e-6) / 1e9
+            entry = {"n_ctx": n_ctx, "num_splits": plan.max_splits, "us": round(us, 3),
+                     "gbs": round(gbs, 1), "schedule": "stream-K" if plan.schedule == 2
+                     else "uniform splits"}
+            if name == "default":
+                default[n_ctx] = entry
+            else:
+                entry["requested_splits"] = name
+                entry["blocks_per_split"] = plan.blocks_per_split
+                sweep.append(entry)
+            log(f"[bench] N={n_ctx} plan {name}: {us:.2f} us, {gbs:.0f} GB/s "
+                f"({entry['num_splits']} splits)")
+        del kbig, vbig, kd, vd
+    best = {}
+    for e in sweep:
+        b = best.get(e["n_ctx"])
+        if b is None or e["us"] < b["us"]:
+            best[e["n_ctx"]] = e
+    top = default[wl.SPLITKV_CONTEXTS[-1]]
+    rec = {
+        "metric": "contiguous split-KV decode KV GB/s (% HBM peak), B=4 H=16 D=64 fp16, N=16384",
+        "value": top["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(top["us"] / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "split-KV decode over contiguous caches (NULL block table): "
+                               "4 sequences, Hq = Hkv = 16, d = 64, fp16, one query row",
+                   "n_ctx": list(wl.SPLITKV_CONTEXTS), "num_splits": list(wl.SPLITKV_SPLITS),
+                   "cache": f"rotating copies, >= {args.pool_bytes / 2**20:.0f} MiB per N"},
+        "roofline": {"bound": "hbm", "achieved": top["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(top["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_sk_kernel (f16, d_pad 64, group 1, block 16)"},
+        "default_plan": [default[n] for n in wl.SPLITKV_CONTEXTS],
+        "best_forced_split": [best[n] for n in wl.SPLITKV_CONTEXTS],
+        "sweep": sweep,
+        "parity_max_abs_err": max(errs),
+        "device": props.name,
+    }
+    if not args.no_cpu_baseline:
+        bst, sample = cpu_baseline(cpu_inp, args.cpu_seconds)
+        rec["cpu_baseline"] = {"value": round(cpu_inp.kv_bytes() / bst / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"N={cpu_inp.context_lens[0].item()}: {sample}"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_fused_prefill(args, dev, props) -> int:
+    """Whole-prompt causal prefill over contiguous caches (past = 0): time and
+    peak device memory per N, next to the bytes a prefill that materialises
+    the [B, H, N, N] scores and probabilities in fp16 would need (derived,
+    not run)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_178_amd import binding
+    from paged_kv_cache_178_amd import workloads as wl
+
+    K = max(1, min(args.steps, 20))
+    rows, errs = [], []
+    for n_ctx in wl.SPLITKV_CONTEXTS:
+        inp = wl.fused_prefill(n_ctx)
+        ns, hq, d = inp.num_seqs, inp.num_q_heads, inp.head_dim
+        flops = causal_flops(inp)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        q = inp.q.to(dev)
+        k = wl.dense_view(inp.k_pool.to(dev), ns)
+        v = wl.dense_view(inp.v_pool.to(dev), ns)
+        lens = inp.context_lens.to(dev)
+        qst = inp.q_start.to(dev)
+        torch.cuda.synchronize()
+        in_bytes = sum(t.numel() * t.element_size() for t in (q, k, v))
+        torch.cuda.reset_peak_memory_stats(dev)
+        before = torch.cuda.memory_allocated(dev)
+        out = torch.empty_like(q)
+        desc = binding.make_desc_contiguous(q, k, out=out, scale=inp.scale)
+        plan = binding.np_plan(desc, inp.context_lens.numpy(), inp.q_start.numpy())
+        ws = binding.workspace_for(plan, dev)
+        binding.np_paged_attention_prefill(desc, plan, q, k, v, None, lens, qst, out, ws)
+        torch.cuda.synchronize()
+        peak_extra = torch.cuda.max_memory_allocated(dev) - before
+        out_bytes = out.numel() * out.element_size()
+        # Sampled rows against the oracle: row t of sequence s is the decode of
+        # query t over keys 0..t of the same cache.
+        rng = np.random.default_rng(n_ctx)
+        got = out.to("cpu", torch.float64).numpy()
+        worst = 0.0
+        for s in range(ns):
+            for t in sorted({0, n_ctx // 2, n_ctx - 1, int(rng.integers(n_ctx))}):
+                r = s * n_ctx + t
+                # Only the blocks row t sees, as a pool of their own.
+                nb_t = t // 16 + 1
+                b0 = int(inp.block_table[s, 0])
+                ref = oracle.paged_attention(inp.q[r:r + 1], inp.k_pool[b0:b0 + nb_t],
+                                             inp.v_pool[b0:b0 + nb_t],
+                                             torch.arange(nb_t, dtype=torch.int32)[None],
+                                             torch.tensor([t + 1], dtype=torch.int32),
+                                             scale=inp.scale)
+                err = np.abs(got[r:r + 1] - ref)
+                if not (err <= 1e-2 + 1e-2 * np.abs(ref)).all():
+                    print(f"bench.py: parity gate failed at N={n_ctx}, row {r}: max abs err "
+                          f"{err.max():.3e}", file=sys.stderr)
+                    return 1
+                worst = max(worst, float(err.max()))
+        errs.append(worst)
+
+        def step(i):
+            binding.np_paged_attention_prefill(desc, plan, q, k, v, None, lens, qst, out, ws)
+
+        for i in range(min(args.warmup, 3)):
+            step(i)
+        us = graph_us(step, K)
+        tfs = flops / (us * 1e-6) / 1e12
+        naive = 2 * ns * hq * n_ctx * n_ctx * 2
+        rows.append({"n_ctx": n_ctx, "us": round(us, 2), "tflops": round(tfs, 1),
+                     "inputs_bytes": in_bytes, "output_bytes": out_bytes,
+                     "workspace_bytes": plan.workspace_bytes,
+                     "peak_bytes_during_call": peak_extra,
+                     "peak_total_bytes": in_bytes + peak_extra,
+                     "naive_scores_and_probs_bytes": naive,
+                     "naive_peak_bytes": in_bytes + out_bytes + naive})
+        log(f"[bench] N={n_ctx}: {us:.1f} us, {tfs:.0f} TFLOP/s; peak {in_bytes + peak_extra} B "
+            f"(inputs {in_bytes}, during the call {peak_extra}); naive would hold "
+            f"{in_bytes + out_bytes + naive} B")
+        del q, k, v, out, ws
+    at = next(r for r in rows if r["n_ctx"] == 4096)
+    rec = {
+        "metric": "fused causal prefill over contiguous caches TFLOP/s, B=4 H=16 D=64 fp16, "
+                  "N=4096 (peak memory per N in 'memory')",
+        "value": at["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": min(args.warmup, 3), "ms_per_step": round(at["us"] / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "whole-prompt causal prefill (past = 0), 4 sequences, Hq = Hkv "
+                               "= 16, d = 64, fp16, NULL block table",
+                   "n_ctx": list(wl.SPLITKV_CONTEXTS)},
+        "roofline": {"bound": "mfma", "achieved": at["tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(at["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_prefill_kernel (f16, d 64, block 16)"},
+        "memory": rows,
+        "parity": "4 sampled rows per sequence per N against the oracle",
+        "parity_max_abs_err": max(errs),
+        "device": props.name,
+        "cpu_baseline": None,
+    }
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -119,9 +119,10 @@ typedef struct np_plan_opts {
                                      the same launch; 1: a separate combine
                                      kernel does it                            */
   int32_t schedule;               /* decode work split: 0 auto (stream-K when
-                                     num_seqs > 1 and nothing above asks for
-                                     uniform splits), 1 uniform splits, 2
-                                     stream-K                                  */
+                                     num_seqs > 1, the longest sequence has
+                                     more than 1.25x the mean blocks, and
+                                     nothing above asks for uniform splits),
+                                     1 uniform splits, 2 stream-K              */
   int32_t segment_cost;           /* stream-K: fixed cost of one (sequence, KV
                                      head), in blocks; 0 => 4                  */
   int32_t reserved;               /* must be 0                                 */

@@ -296,8 +296,19 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
       }
       stream_k = true;
     } else if (o.schedule == 0) {
-      stream_k = c.num_seqs > 1 && c.num_seqs <= kSkMaxSeqs && o.force_blocks_per_split == 0 &&
-                 o.combine_mode == 0 && u_bound < (int64_t(1) << 30);
+      // Stream-K pays off when the lengths are ragged (uniform splits then
+      // leave a tail of long sequences); for equal lengths uniform splits are
+      // already balanced and need no merge of shared segments.
+      int64_t sum_nb = 0, max_nb = 0;
+      for (int32_t s = 0; s < c.num_seqs; ++s) {
+        const int64_t nb = ceil_div(lens[s], c.block_size);
+        sum_nb += nb;
+        max_nb = std::max(max_nb, nb);
+      }
+      const bool ragged = max_nb * 4 * c.num_seqs > sum_nb * 5;   // max > 1.25 x mean
+      stream_k = c.num_seqs > 1 && ragged && c.num_seqs <= kSkMaxSeqs &&
+                 o.force_blocks_per_split == 0 && o.combine_mode == 0 &&
+                 u_bound < (int64_t(1) << 30);
     }
     c.sk_cost = stream_k ? cost : 0;
   }

@@ -301,7 +301,11 @@ def test_stream_k_plan_matches_model(seed):
 def test_schedule_selection():
     lens = np.array([4096, 100, 7], np.int32)
     d = desc(num_seqs=3, hq=32, hkv=8, max_blocks=256, n_blocks=600)
-    assert B.np_plan(d, lens).schedule == 2                     # auto, batch > 1
+    assert B.np_plan(d, lens).schedule == 2                     # auto, ragged batch
+    # Equal lengths (or nearly: max <= 1.25 x mean blocks) keep uniform splits.
+    assert B.np_plan(d, np.array([4096, 4096, 4096], np.int32)).schedule == 1
+    assert B.np_plan(d, np.array([4096, 3500, 3300], np.int32)).schedule == 1
+    assert B.np_plan(d, np.array([4096, 2000, 3300], np.int32)).schedule == 2
     assert B.np_plan(d, lens, None, B.PlanOpts(schedule=1)).schedule == 1
     assert B.np_plan(d, lens, None, B.PlanOpts(combine_mode=1)).schedule == 1
     assert B.np_plan(d, lens, None, B.PlanOpts(force_blocks_per_split=8)).schedule == 1
