@@ -78,6 +78,19 @@ def test_stream_k_other_shapes(maker):
     _run_parity(maker(), binding.PlanOpts(schedule=2))
 
 
+@pytest.mark.parametrize("num_seqs", [65, 130, 2048])
+def test_stream_k_many_sequences(num_seqs):
+    """The device scan of the lengths runs 64 sequences per pass with a carry
+    between passes; 65 and 130 sequences cross pass boundaries, 2048 is the
+    largest batch the stream-K kernel takes."""
+    rng = np.random.default_rng(44 + num_seqs)
+    top = 600 if num_seqs < 2048 else 48
+    lens = rng.integers(1, top, size=num_seqs).tolist()
+    lens[num_seqs // 3] = top * 4                      # one long sequence
+    inp = wl.custom(45 + num_seqs, lens, hq=8, hkv=4, d=64, dtype="bf16")
+    _run_parity(inp, binding.PlanOpts(schedule=2))
+
+
 def test_stream_k_follows_device_lengths():
     """The stream-K kernel derives its schedule from the device lengths: a
     plan made for other lengths (same batch) still computes the attention
