@@ -264,13 +264,13 @@ __device__ __forceinline__ float2 fetch2(const float* p) {
 // Latency-parallel: waves take splits round-robin, each lane owns float4
 // chunks of the G x d_pad output, and a batch of UB splits has all its loads
 // in flight before any is used; the per-wave states are merged through LDS.
-template <int DT, int D_PAD, int G, int UB_MAX = 16, typename PartOf>
+template <int DT, int D_PAD, int G, typename PartOf>
 __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh, int splits,
                                              PartOf&& part_of) {
   constexpr int NW = kDecodeWaves;
   constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
   constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
-  constexpr int UB = CPL > 1 ? (UB_MAX < 8 ? UB_MAX : 8) : UB_MAX;
+  constexpr int UB = CPL > 1 ? 8 : 16;
   const int wave = threadIdx.x / kWaveSize;
   const int lane = threadIdx.x % kWaveSize;
 
