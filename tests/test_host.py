@@ -494,3 +494,14 @@ def test_append_entry_errors_before_launch():
     assert call(pl=None) == S["NP_ERR_BAD_PLAN"]
     assert call(pl=B.np_plan(desc(num_seqs=2, hq=32, hkv=8, max_blocks=256, n_blocks=600),
                              lens)) == S["NP_ERR_BAD_PLAN"]      # a decode plan
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises; there is no
+    CPU fallback behind the binding."""
+    monkeypatch.setattr(B, "_LIB", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        B.library()
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        B.np_plan(desc(), np.array([3, 5], np.int32))
