@@ -210,6 +210,22 @@ def test_edge_lengths(lens):
                           max_blocks=max(-(-x // 16) for x in lens)))
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(schedule=2)], ids=["uniform", "stream_k"])
+def test_long_history_32k(opts):
+    """A 32768-token history (2048 blocks, 64 splits of the default plan)."""
+    _run_parity(wl.custom(46, [32768], hq=32, hkv=8, d=64, dtype="bf16"),
+                binding.PlanOpts(**opts))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_group_and_head_dim(dtype):
+    """The largest built kernel shape: head_dim 128 and 8 query heads per KV
+    head, over ragged lengths, both schedules."""
+    inp = wl.custom(47, [8192, 3000, 17], hq=64, hkv=8, d=128, dtype=dtype)
+    _run_parity(inp, binding.PlanOpts(schedule=1))
+    _run_parity(inp, binding.PlanOpts(schedule=2))
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 5, 6, 7, 8])
 def test_groups(group):
     _run_parity(wl.custom(16 + group, [700, 45], hq=2 * group, hkv=2, d=64, dtype="bf16"))
