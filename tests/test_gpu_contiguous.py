@@ -129,3 +129,45 @@ def test_append_contiguous_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(kd.cpu().view(torch.int16).numpy(), want_k)
     assert np.array_equal(vd.cpu().view(torch.int16).numpy(), want_v)
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(force_blocks_per_split=128)],
+                         ids=["default", "8_splits"])
+def test_splitkv_full_size_16k(opts):
+    """The largest context of the split-KV sweep, in the plans the benchmark
+    times (the planner's default and the best forced split), against the full
+    oracle."""
+    inp = wl.splitkv_decode(16384)
+    print(f"[contiguous decode] {inp.name} opts={opts}", flush=True)
+    got, _ = dense_decode(inp, B.PlanOpts(**opts))
+    H.assert_close(got, H.oracle_out(inp), "f16", inp.name)
+
+
+def test_fused_prefill_full_size_sampled():
+    """The benchmark's 4 x 4096 whole-prompt prefill; sampled rows checked one
+    by one (row t of sequence s is the decode of query t over keys 0..t)."""
+    inp = wl.fused_prefill(4096)
+    dev = H.to_device(inp)
+    k = wl.dense_view(dev["k_pool"], inp.num_seqs)
+    v = wl.dense_view(dev["v_pool"], inp.num_seqs)
+    out = torch.empty_like(dev["q"])
+    desc = B.make_desc_contiguous(dev["q"], k, out=out, scale=inp.scale)
+    plan = B.np_plan(desc, inp.context_lens, inp.q_start)
+    print(f"[contiguous prefill] {inp.name}", flush=True)
+    B.np_paged_attention_prefill(desc, plan, dev["q"], k, v, None, dev["context_lens"],
+                                 dev["q_start"], out, B.workspace_for(plan, "cuda"))
+    torch.cuda.synchronize()
+    got = out.cpu()
+    rng = np.random.default_rng(63)
+    n = 4096
+    for s in range(inp.num_seqs):
+        for t in sorted({0, 1, 63, 64, n // 2, n - 1, *rng.integers(n, size=4).tolist()}):
+            r = s * n + t
+            b0 = int(inp.block_table[s, 0])
+            nb_t = t // 16 + 1
+            ref = oracle.paged_attention(inp.q[r:r + 1], inp.k_pool[b0:b0 + nb_t],
+                                         inp.v_pool[b0:b0 + nb_t],
+                                         torch.arange(nb_t, dtype=torch.int32)[None],
+                                         torch.tensor([t + 1], dtype=torch.int32),
+                                         scale=inp.scale)
+            H.assert_close(got[r:r + 1], ref, "f16", f"seq {s} row {t}")
