@@ -176,7 +176,8 @@ np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
  * piece to finish, in the same launch. The kernel recomputes the schedule
  * from the device context_lens. At most 2048 sequences;
  * force_blocks_per_split and combine_mode 1 select uniform splits.
- * Prefill: one workgroup per (sequence, KV head, tile of query rows).
+ * Prefill: one workgroup per (sequence, KV head, tile of query rows), the
+ * tiles of later rows (more keys under the causal mask) launched first.
  *
  * On success *out owns a new plan; the caller releases it with
  * np_plan_destroy after the last launch that uses it.

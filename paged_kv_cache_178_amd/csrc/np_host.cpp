@@ -399,7 +399,8 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     for (int32_t s = 0; s < c.num_seqs; ++s) {
       const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
       for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
-        const int64_t tile = x / c.hkv, kvh = x % c.hkv;
+        // Largest (latest, causally longest) tiles are launched first.
+        const int64_t tile = max_tiles - 1 - x / c.hkv, kvh = x % c.hkv;
         if (tile >= tiles[s]) continue;
         // Rows covered by the tile's units (clipped to the chunk).
         const int64_t u0 = tile * kPrefillUnits;

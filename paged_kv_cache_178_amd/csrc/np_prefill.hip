@@ -134,7 +134,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][NG][kVTile];
 
   const int kvh = blockIdx.x % p.hkv;
-  const int tile = blockIdx.x / p.hkv;
+  // Tiles are launched largest first: later query rows see more keys under the
+  // causal mask, so the longest workgroups start first and the shortest fill
+  // the end of the launch (x runs over tiles in descending order).
+  const int tile = int(gridDim.x) / p.hkv - 1 - int(blockIdx.x) / p.hkv;
   const int s = blockIdx.y;
   const int G = p.group;
   const int row0 = p.q_start[s];

@@ -169,7 +169,7 @@ def model_prefill_plan(q_start, hq, hkv, rows=64, waves=4):
     for s, n in enumerate(n_qs):
         units = g * math.ceil(n / rows)
         for x in range(max_tiles * hkv):
-            tile, kvh = divmod(x, hkv)
+            tile, kvh = max_tiles - 1 - x // hkv, x % hkv     # largest tiles first
             if tile >= tiles[s]:
                 continue
             u0, u1 = tile * waves, min(tile * waves + waves, units)
