@@ -746,8 +746,17 @@ def run_fused_prefill(args, dev, props) -> int:
         "parity": "4 sampled rows per sequence per N against the oracle",
         "parity_max_abs_err": max(errs),
         "device": props.name,
-        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        small = wl.fused_prefill(1024)
+        best, sample = cpu_baseline(small, args.cpu_seconds, seqs=[0], prefill=True)
+        sub = wl.PagedInputs(**{**small.__dict__, "context_lens": small.context_lens[:1],
+                                "q_start": small.q_start[:2]})
+        rec["cpu_baseline"] = {"value": round(causal_flops(sub) / best / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": f"one 1024-token prompt: {sample}"}
+    else:
+        rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
     return 0
 
