@@ -791,10 +791,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 //
 // For ragged batches. A workgroup serves HW KV heads at once (HW = 4, 2 or 1,
 // the largest that divides Hkv): its wave k takes head k % HW, and the
-// NW / HW waves of one head take alternate blocks. So the workgroup reads HW
-// consecutive heads of every slot of a block together -- HW x 128 bytes in one
-// run for 16-bit d = 64 -- which streams from HBM markedly faster than one
-// head's row per slot spread over separate workgroups.
+// NW / HW waves of one head take alternate blocks. So the HW heads of a block
+// (4 x 128 contiguous bytes per slot for 16-bit d = 64) are fetched by one
+// workgroup at about the same time, rather than a head at a time by separate
+// workgroups far apart in the launch; a read probe over the batching pool
+// streams the first pattern about 15% faster than the second.
 //
 // Every (sequence, head group) is a segment of nb_s block units followed by
 // sk_cost virtual units that stand for the fixed cost of a segment (its q
