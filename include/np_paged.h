@@ -180,7 +180,9 @@ np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
  * tiles of later rows (more keys under the causal mask) launched first.
  *
  * On success *out owns a new plan; the caller releases it with
- * np_plan_destroy after the last launch that uses it.
+ * np_plan_destroy after the last launch that uses it. Planning costs
+ * O(num_seqs) host work; the work-item list of the accessors below is built
+ * on their first call (thread-safe) and kept with the plan.
  */
 np_status np_plan(const np_paged_desc* desc, const int32_t* context_lens_host,
                   const int32_t* q_start_host, const np_plan_opts* opts,

@@ -171,23 +171,20 @@ namespace np {
 namespace {
 
 // Stream-K decode schedule (the kernel recomputes it on the device from the
-// lengths it reads; this copy sizes the launch and lists the pieces). A
-// workgroup serves HW = sk_heads_per_wg(Hkv) KV heads at once; each
-// (sequence, head group) is a segment of its blocks plus sk_cost virtual
-// units; segments in (sequence, head group) order, U units in all, W
-// workgroups of C = ceil(U / W) consecutive units. A piece is the part of a
-// segment's blocks inside one workgroup's range; it is listed once per KV
-// head of the group.
-void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
-                   std::vector<int32_t>& items) {
+// lengths it reads; this copy sizes the launch). A workgroup serves
+// HW = sk_heads_per_wg(Hkv) KV heads at once; each (sequence, head group) is
+// a segment of its blocks plus sk_cost virtual units; segments in (sequence,
+// head group) order, U units in all, W workgroups of C = ceil(U / W)
+// consecutive units. A piece is the part of a segment's blocks inside one
+// workgroup's range.
+void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o) {
   const int64_t cost = c.sk_cost;
   const int64_t hw = sk_heads_per_wg(c.hkv);
   const int64_t n_hg = c.hkv / hw;
-  std::vector<int64_t> nb(c.num_seqs);
   int64_t U = 0;
   for (int32_t s = 0; s < c.num_seqs; ++s) {
-    nb[s] = std::min<int64_t>(ceil_div(lens[s], c.block_size), c.max_blocks);
-    U += (nb[s] + cost) * n_hg;
+    const int64_t nb = std::min<int64_t>(ceil_div(lens[s], c.block_size), c.max_blocks);
+    U += (nb + cost) * n_hg;
   }
   const int64_t num_cus = o.num_cus ? o.num_cus : 256;
   const int64_t per_cu = o.wgs_per_cu ? o.wgs_per_cu : kSkWgsPerCu;
@@ -195,28 +192,17 @@ void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
   int64_t W = std::min(num_cus * per_cu, ceil_div(U, min_units));
   W = std::max<int64_t>(1, std::min(W, U));
   const int64_t C = ceil_div(U, W);
+  // The most pieces of one segment.
   int64_t max_pieces = 1;
   int64_t seg_start = 0;
-  // Pieces by workgroup, in unit order; built segment by segment.
-  std::vector<std::vector<int32_t>> by_wg(W);
   for (int32_t s = 0; s < c.num_seqs; ++s) {
+    const int64_t nb = std::min<int64_t>(ceil_div(lens[s], c.block_size), c.max_blocks);
     for (int64_t hg = 0; hg < n_hg; ++hg) {
-      const int64_t real_end = seg_start + std::max<int64_t>(nb[s], 1);
-      const int64_t w_first = seg_start / C, w_last = (real_end - 1) / C;
-      max_pieces = std::max(max_pieces, w_last - w_first + 1);
-      for (int64_t w = w_first; w <= w_last; ++w) {
-        const int64_t lo = std::max(seg_start, w * C) - seg_start;
-        const int64_t hi = std::min(real_end, (w + 1) * C) - seg_start;
-        for (int64_t k = 0; k < hw; ++k) {
-          const int32_t item[5] = {s, int32_t(hg * hw + k), int32_t(w), int32_t(lo),
-                                   int32_t(std::min<int64_t>(hi, nb[s]))};
-          by_wg[w].insert(by_wg[w].end(), item, item + 5);
-        }
-      }
-      seg_start += nb[s] + cost;
+      const int64_t real_end = seg_start + std::max<int64_t>(nb, 1);
+      max_pieces = std::max(max_pieces, (real_end - 1) / C - seg_start / C + 1);
+      seg_start += nb + cost;
     }
   }
-  for (const auto& v : by_wg) items.insert(items.end(), v.begin(), v.end());
   c.schedule = kScheduleStreamK;
   c.blocks_per_split = static_cast<int32_t>(C);
   c.max_splits = static_cast<int32_t>(max_pieces);
@@ -236,6 +222,71 @@ void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o,
   c.ws_ml_off = round(size_t(c.num_seqs) * c.hkv * kCounterStride * sizeof(uint32_t));
   c.ws_acc_off = c.ws_ml_off + round(n_part * 2 * sizeof(float));
   c.ws_bytes = c.ws_acc_off + round(n_part * c.d_pad * sizeof(float));
+}
+
+// The work-item list of a plan, in launch order of the active workgroups
+// (5 ints each: sequence, KV head, split / workgroup / tile, first, end).
+void build_items(const np_plan_s& plan, std::vector<int32_t>& items) {
+  const np_plan_core& c = plan.core;
+  const int32_t* lens = plan.lens.data();
+  auto add = [&](int64_t a, int64_t b, int64_t d, int64_t e, int64_t f) {
+    const int32_t item[5] = {int32_t(a), int32_t(b), int32_t(d), int32_t(e), int32_t(f)};
+    items.insert(items.end(), item, item + 5);
+  };
+  if (c.is_prefill) {
+    // One workgroup per (sequence, KV head, tile); a tile is kPrefillUnits
+    // units, a unit one query head times kPrefillRowsPerWave rows, units
+    // numbered head-fastest; the largest tiles are launched first.
+    const int32_t* qs = plan.q_start.data();
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t n_q = int64_t(qs[s + 1]) - qs[s];
+      const int64_t units = c.group * ceil_div(n_q, kPrefillRowsPerWave);
+      const int64_t tiles = ceil_div(units, kPrefillUnits);
+      for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
+        const int64_t tile = c.max_tiles - 1 - x / c.hkv, kvh = x % c.hkv;
+        if (tile >= tiles) continue;
+        const int64_t u0 = tile * kPrefillUnits;
+        const int64_t u1 = std::min<int64_t>(u0 + kPrefillUnits, units);
+        const int64_t r0 = (u0 / c.group) * kPrefillRowsPerWave;
+        const int64_t r1 = std::min<int64_t>(((u1 - 1) / c.group + 1) * kPrefillRowsPerWave, n_q);
+        add(s, kvh, tile, r0, r1);
+      }
+    }
+  } else if (c.schedule == kScheduleStreamK) {
+    const int64_t cost = c.sk_cost, hw = sk_heads_per_wg(c.hkv), n_hg = c.hkv / hw;
+    const int64_t W = c.grid[0], C = c.blocks_per_split;
+    std::vector<std::vector<int32_t>> by_wg(W);
+    int64_t seg_start = 0;
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t nb = std::min<int64_t>(ceil_div(lens[s], c.block_size), c.max_blocks);
+      for (int64_t hg = 0; hg < n_hg; ++hg) {
+        const int64_t real_end = seg_start + std::max<int64_t>(nb, 1);
+        for (int64_t w = seg_start / C; w <= (real_end - 1) / C; ++w) {
+          const int64_t lo = std::max(seg_start, w * C) - seg_start;
+          const int64_t hi = std::min(real_end, (w + 1) * C) - seg_start;
+          for (int64_t k = 0; k < hw; ++k) {
+            const int32_t item[5] = {s, int32_t(hg * hw + k), int32_t(w), int32_t(lo),
+                                     int32_t(std::min<int64_t>(hi, nb))};
+            by_wg[w].insert(by_wg[w].end(), item, item + 5);
+          }
+        }
+        seg_start += nb + cost;
+      }
+    }
+    for (const auto& v : by_wg) items.insert(items.end(), v.begin(), v.end());
+  } else {
+    // Uniform splits: blocks_per_split consecutive blocks per split.
+    const int64_t bps = c.blocks_per_split;
+    for (int32_t s = 0; s < c.num_seqs; ++s) {
+      const int64_t nb = ceil_div(lens[s], c.block_size);
+      const int64_t splits = ceil_div(nb, bps);
+      for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
+        const int64_t split = x / c.hkv, kvh = x % c.hkv;
+        if (split >= splits) continue;
+        add(s, kvh, split, split * bps, std::min<int64_t>(split * bps + bps, nb));
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -312,8 +363,10 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     }
     c.sk_cost = stream_k ? cost : 0;
   }
+  plan->lens.assign(lens, lens + c.num_seqs);
+  if (q_start) plan->q_start.assign(q_start, q_start + c.num_seqs + 1);
   if (stream_k) {
-    plan_stream_k(c, lens, o, plan->items);
+    plan_stream_k(c, lens, o);
   } else if (!c.is_prefill) {
     // Split-KV decode ("2. Split-KV flash-decoding"): page-aligned splits of a
     // uniform number of blocks, so that no split is empty and each workgroup
@@ -344,19 +397,7 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     c.grid[1] = static_cast<uint32_t>(c.num_seqs);
     c.grid[2] = 1;
     c.wg_size = kDecodeWaves * kWaveSize;
-    bool any_split = false;
-    for (int32_t s = 0; s < c.num_seqs; ++s) {
-      const int64_t splits = ceil_div(ceil_div(lens[s], c.block_size), bps);
-      any_split = any_split || splits > 1;
-      for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
-        const int64_t split = x / c.hkv, kvh = x % c.hkv;
-        if (split >= splits) continue;
-        const int64_t b0 = split * bps;
-        const int64_t b1 = std::min<int64_t>(b0 + bps, ceil_div(lens[s], c.block_size));
-        const int32_t item[5] = {s, int32_t(kvh), int32_t(split), int32_t(b0), int32_t(b1)};
-        plan->items.insert(plan->items.end(), item, item + 5);
-      }
-    }
+    const bool any_split = c.max_splits > 1;
     c.fused_combine = any_split && o.combine_mode == 0;
     c.combine_wgs =
         (any_split && !c.fused_combine) ? static_cast<uint32_t>(c.num_seqs * c.hkv) : 0;
@@ -376,13 +417,11 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     // kPrefillRowsPerWave query rows. Units are numbered head-fastest. Each
     // unit has two waves, which take alternate key tiles.
     int64_t max_tiles = 0, max_rows = 0;
-    std::vector<int64_t> tiles(c.num_seqs);
     for (int32_t s = 0; s < c.num_seqs; ++s) {
       const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
       max_rows = std::max(max_rows, n_q);
       const int64_t units = c.group * ceil_div(n_q, kPrefillRowsPerWave);
-      tiles[s] = ceil_div(units, kPrefillUnits);
-      max_tiles = std::max(max_tiles, tiles[s]);
+      max_tiles = std::max(max_tiles, ceil_div(units, kPrefillUnits));
     }
     c.schedule = 0;
     c.blocks_per_split = 0;
@@ -396,22 +435,6 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
     c.combine_wgs = 0;
     c.fused_combine = 0;
     c.ws_cnt_off = c.ws_ml_off = c.ws_acc_off = c.ws_bytes = 0;
-    for (int32_t s = 0; s < c.num_seqs; ++s) {
-      const int64_t n_q = int64_t(q_start[s + 1]) - q_start[s];
-      for (int64_t x = 0; x < int64_t(c.grid[0]); ++x) {
-        // Largest (latest, causally longest) tiles are launched first.
-        const int64_t tile = max_tiles - 1 - x / c.hkv, kvh = x % c.hkv;
-        if (tile >= tiles[s]) continue;
-        // Rows covered by the tile's units (clipped to the chunk).
-        const int64_t u0 = tile * kPrefillUnits;
-        const int64_t u1 = std::min<int64_t>(u0 + kPrefillUnits,
-                                             c.group * ceil_div(n_q, kPrefillRowsPerWave));
-        const int64_t r0 = (u0 / c.group) * kPrefillRowsPerWave;
-        const int64_t r1 = std::min<int64_t>(((u1 - 1) / c.group + 1) * kPrefillRowsPerWave, n_q);
-        const int32_t item[5] = {s, int32_t(kvh), int32_t(tile), int32_t(r0), int32_t(r1)};
-        plan->items.insert(plan->items.end(), item, item + 5);
-      }
-    }
   }
   *out = plan;
   return NP_OK;
@@ -444,14 +467,21 @@ int32_t np_plan_is_prefill(const np_plan_t* p) {
   return (p && p->magic == kPlanMagic) ? p->core.is_prefill : -1;
 }
 
+// The work-item list is built once, on the first accessor call.
+static const std::vector<int32_t>& plan_items(const np_plan_t* p) {
+  std::call_once(p->items_once, [p] { build_items(*p, p->items); });
+  return p->items;
+}
+
 int64_t np_plan_num_work_items(const np_plan_t* p) {
-  return (p && p->magic == kPlanMagic) ? int64_t(p->items.size() / 5) : -1;
+  return (p && p->magic == kPlanMagic) ? int64_t(plan_items(p).size() / 5) : -1;
 }
 
 np_status np_plan_work_item(const np_plan_t* p, int64_t index, int32_t item[5]) {
   if (p == nullptr || p->magic != kPlanMagic || item == nullptr) return NP_ERR_NULL_PTR;
-  if (index < 0 || index >= int64_t(p->items.size() / 5)) return NP_ERR_BAD_SHAPE;
-  std::memcpy(item, p->items.data() + index * 5, 5 * sizeof(int32_t));
+  const std::vector<int32_t>& items = plan_items(p);
+  if (index < 0 || index >= int64_t(items.size() / 5)) return NP_ERR_BAD_SHAPE;
+  std::memcpy(item, items.data() + index * 5, 5 * sizeof(int32_t));
   return NP_OK;
 }
 

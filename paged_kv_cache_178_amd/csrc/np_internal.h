@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "np_paged.h"
@@ -61,7 +62,13 @@ struct np_plan_core {
 struct np_plan_s {
   uint32_t magic;
   np::np_plan_core core;
-  std::vector<int32_t> items;   // 5 ints per active workgroup, launch order
+  // The host lengths (and query starts) the plan was made for: launches need
+  // only `core`; the work-item list, for inspection, is derived from these on
+  // the first accessor call, so planning stays O(sequences).
+  std::vector<int32_t> lens;
+  std::vector<int32_t> q_start;
+  mutable std::once_flag items_once;
+  mutable std::vector<int32_t> items;   // 5 ints per active workgroup, launch order
 };
 
 namespace np {
