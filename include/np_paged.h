@@ -120,7 +120,9 @@ typedef struct np_plan_opts {
                                      kernel does it                            */
   int32_t schedule;               /* decode work split: 0 auto (stream-K when
                                      num_seqs > 1, the longest sequence has
-                                     more than 1.25x the mean blocks, and
+                                     more than 1.25x the mean blocks, the
+                                     stream-K launch would be full (U >=
+                                     num_cus * wgs_per_cu * min_units), and
                                      nothing above asks for uniform splits),
                                      1 uniform splits, 2 stream-K              */
   int32_t segment_cost;           /* stream-K: fixed cost of one (sequence, KV

@@ -357,7 +357,16 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
         max_nb = std::max(max_nb, nb);
       }
       const bool ragged = max_nb * 4 * c.num_seqs > sum_nb * 5;   // max > 1.25 x mean
-      stream_k = c.num_seqs > 1 && ragged && c.num_seqs <= kSkMaxSeqs &&
+      // ... and when the batch has enough blocks to give every workgroup of
+      // the stream-K launch its least share; a small batch runs faster as
+      // many small uniform splits.
+      const int64_t hw = sk_heads_per_wg(c.hkv);
+      const int64_t units = (sum_nb + int64_t(c.num_seqs) * cost) * (c.hkv / hw);
+      const int64_t slots = int64_t(o.num_cus ? o.num_cus : 256) *
+                            (o.wgs_per_cu ? o.wgs_per_cu : kSkWgsPerCu);
+      const int64_t least = o.min_blocks_per_split ? o.min_blocks_per_split : kSkMinUnits;
+      const bool fills = units >= slots * least;
+      stream_k = c.num_seqs > 1 && ragged && fills && c.num_seqs <= kSkMaxSeqs &&
                  o.force_blocks_per_split == 0 && o.combine_mode == 0 &&
                  u_bound < (int64_t(1) << 30);
     }

@@ -109,14 +109,15 @@ def test_stream_k_follows_device_lengths():
     assert int(ws[: 256 * 4 * 8].view(torch.int32).abs().sum()) == 0
 
 
-def test_workspace_reuse_keeps_counters_zero():
+@pytest.mark.parametrize("schedule", [1, 2])
+def test_workspace_reuse_keeps_counters_zero(schedule):
     """The same workspace serves repeated calls: the arrival counters are left
     at zero by every call and the outputs repeat bit for bit."""
     inp = wl.custom(40, [4096, 3000, 100], hq=32, hkv=8, d=64, dtype="bf16")
     dev = H.to_device(inp)
     desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], scale=inp.scale)
-    plan = binding.np_plan(desc, inp.context_lens)
-    assert plan.schedule == 2
+    plan = binding.np_plan(desc, inp.context_lens, None, binding.PlanOpts(schedule=schedule))
+    assert plan.schedule == schedule
     ws = binding.workspace_for(plan, "cuda")
     outs = []
     for _ in range(3):

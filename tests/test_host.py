@@ -301,11 +301,20 @@ def test_stream_k_plan_matches_model(seed):
 def test_schedule_selection():
     lens = np.array([4096, 100, 7], np.int32)
     d = desc(num_seqs=3, hq=32, hkv=8, max_blocks=256, n_blocks=600)
-    assert B.np_plan(d, lens).schedule == 2                     # auto, ragged batch
-    # Equal lengths (or nearly: max <= 1.25 x mean blocks) keep uniform splits.
-    assert B.np_plan(d, np.array([4096, 4096, 4096], np.int32)).schedule == 1
-    assert B.np_plan(d, np.array([4096, 3500, 3300], np.int32)).schedule == 1
-    assert B.np_plan(d, np.array([4096, 2000, 3300], np.int32)).schedule == 2
+    # A small ragged batch: too little work to fill the stream-K launch.
+    assert B.np_plan(d, lens).schedule == 1
+    # A large ragged batch (the continuous-batching shape) takes stream-K;
+    # equal lengths (or nearly: max <= 1.25 x mean blocks) keep uniform splits.
+    rng = np.random.default_rng(4)
+    big = rng.integers(128, 8192, size=64, endpoint=True).astype(np.int32)
+    db = desc(num_seqs=64, hq=32, hkv=8, max_blocks=512, n_blocks=40000)
+    assert B.np_plan(db, big).schedule == 2
+    assert B.np_plan(db, np.full(64, 4096, np.int32)).schedule == 1
+    near = np.full(64, 4096, np.int32)
+    near[::2] = 3500
+    assert B.np_plan(db, near).schedule == 1
+    # The fill test follows the launch options: on 16 CUs the small batch fills it.
+    assert B.np_plan(d, lens, None, B.PlanOpts(num_cus=16)).schedule == 2
     assert B.np_plan(d, lens, None, B.PlanOpts(schedule=1)).schedule == 1
     assert B.np_plan(d, lens, None, B.PlanOpts(combine_mode=1)).schedule == 1
     assert B.np_plan(d, lens, None, B.PlanOpts(force_blocks_per_split=8)).schedule == 1
