@@ -9,9 +9,11 @@ scattered over a pool twice the size the history needs.
 A step is one decode call through the C ABI: the split-KV decode kernel with
 its in-launch split merge, on a plan and workspace prepared once (the plan
 stays valid while the lengths keep the same split layout). The timed region
-replays a HIP graph of K steps; each step reads a different copy of the
-pool, and the copies together exceed 1 GiB, so the 256 MiB Infinity Cache
-cannot serve the KV stream from one step to the next (cold HBM).
+replays a HIP graph of K steps; step i reads copy i mod 64 of the pool (1 GiB
+of copies), and a 512 MiB read of an unrelated buffer runs between the
+untimed warm-up replay and the timed one. So every timed step reads K/V that
+at least 504 MiB of other reads have passed through since it was last
+touched, twice the 256 MiB Infinity Cache: cold HBM at any K.
 
 Printed: one JSON line with KV GB/s (whole job), microseconds per step, the
 decode kernel's roofline against 8 TB/s HBM and the float64 oracle's
@@ -24,6 +26,12 @@ Other workloads (not the headline, one JSON line each):
   --workload prefill   4 sequences x (2048 cached + 512 new rows), causal, Llama
                        head shape; TFLOP/s of the exact causal FLOP count
                        against the 2.5 PFLOP/s dense bf16 MFMA peak.
+  --workload read-ceiling
+                       the single-launch ceiling of a plain read of the
+                       headline's 8 MiB: the stream-read probe over 256 ..
+                       2048 workgroups of 256 threads (and 512 and 1024
+                       threads at 256 workgroups) with 1 .. 16 loads of 16 B
+                       in flight per thread, graph-timed on cold copies.
 """
 
 from __future__ import annotations
@@ -84,7 +92,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", choices=("decode", "batching", "tiny", "awkward", "prefill",
-                                           "append", "splitkv", "fused-prefill"),
+                                           "append", "splitkv", "fused-prefill",
+                                           "read-ceiling"),
                     default="decode")
     ap.add_argument("--history", type=int, default=4096)
     ap.add_argument("--pool-bytes", type=float, default=float(1 << 30),
@@ -106,10 +115,47 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def cpu_baseline(inp, seconds: float, seqs=None, prefill=False):
+def host_cores():
+    """(cores this process may run on, cores of the machine)."""
+    return len(os.sched_getaffinity(0)), os.cpu_count()
+
+
+def time_runs(fn, seconds: float, clock=time.perf_counter, min_runs: int = 3):
+    """Call fn until `seconds` of clock time have passed (at least min_runs
+    calls); returns the duration of each call."""
+    times = []
+    t_end = clock() + seconds
+    while clock() < t_end or len(times) < min_runs:
+        t0 = clock()
+        fn()
+        times.append(clock() - t0)
+    return times
+
+
+def run_stats(times):
+    """Best-of is the headline; median and mean show the spread."""
+    xs = sorted(times)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"best": xs[0], "median": med, "mean": sum(xs) / n, "runs": n}
+
+
+def per_step_us(elapsed_ms: float, steps: int) -> float:
+    """Microseconds per step from an event interval (ms) around `steps` steps."""
+    return elapsed_ms * 1e3 / steps
+
+
+def rate(units: float, us: float, scale: float = 1e9) -> float:
+    """units per second / scale (GB/s for bytes with scale 1e9) from µs."""
+    return units / (us * 1e-6) / scale
+
+
+def cpu_baseline(inp, seconds: float, seqs=None, prefill=False, threads=None):
     """Time the float64 oracle (gather, then dense softmax attention) on the
     same workload, or on the sequences `seqs` of it; best-of, the inputs
-    already converted to float64. Returns seconds per call and a description."""
+    already converted to float64, BLAS on `threads` threads (default: every
+    core this process may use). Returns seconds per call, a description and
+    the thread count."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -128,23 +174,49 @@ def cpu_baseline(inp, seconds: float, seqs=None, prefill=False):
         bt = bt[list(seqs)]
         lens = lens[list(seqs)]
         qs = np.concatenate([[0], np.cumsum(n_q)])
-    times = []
-    with threadpool_limits(limits=1):
-        t_end = time.perf_counter() + seconds
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            oracle.paged_attention(q, k, v, bt, lens, q_start=qs if prefill else None,
-                                   scale=inp.scale)
-            times.append(time.perf_counter() - t0)
-    best = min(times)
+    if threads is None:
+        threads = host_cores()[0]
+    with threadpool_limits(limits=threads):
+        times = time_runs(lambda: oracle.paged_attention(
+            q, k, v, bt, lens, q_start=qs if prefill else None, scale=inp.scale), seconds)
+    st = run_stats(times)
     what = "full workload" if seqs is None else f"sequences {list(seqs)} of the workload"
-    desc = (f"{what}, float64 numpy, 1 BLAS thread, best of {len(times)} runs "
-            f"(median {sorted(times)[len(times) // 2] * 1e3:.2f} ms) in {sum(times):.1f} s")
-    return best, desc
+    desc = (f"{what}, float64 numpy, {threads} BLAS thread{'s' if threads > 1 else ''}, "
+            f"best of {st['runs']} runs (median {st['median'] * 1e3:.2f} ms) in "
+            f"{sum(times):.1f} s")
+    return st["best"], desc, threads
+
+
+def cpu_record(value, unit, desc, threads, **extra):
+    """The cpu_baseline object: `cores` is the BLAS thread count used."""
+    avail, total = host_cores()
+    rec = {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "sample": desc,
+           "cores_available": avail, "cpu_count": total}
+    rec.update(extra)
+    return rec
+
+
+_FLUSH = {}
+
+
+def cache_flush() -> None:
+    """Read 512 MiB of an unrelated buffer (twice the Infinity Cache, far more
+    than the L2s), so nothing a timed replay reads is still cached."""
+    import torch
+
+    from paged_kv_cache_178_amd import binding
+
+    dev = torch.cuda.current_device()
+    if dev not in _FLUSH:
+        _FLUSH[dev] = (torch.ones(512 << 20, dtype=torch.uint8, device=dev),
+                       torch.empty(2048 * 256, dtype=torch.int32, device=dev))
+    src, sink = _FLUSH[dev]
+    binding.np_probe_stream_read(src, 2048, sink)
 
 
 def graph_us(fn, n: int) -> float:
-    """Average device time per call of n calls captured in one HIP graph."""
+    """Average device time per call of n calls captured in one HIP graph: one
+    untimed replay, a 512 MiB cache flush, then the timed replay."""
     import torch
 
     graph = torch.cuda.CUDAGraph()
@@ -155,6 +227,7 @@ def graph_us(fn, n: int) -> float:
             fn(i)
     torch.cuda.synchronize()
     graph.replay()
+    cache_flush()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -162,7 +235,7 @@ def graph_us(fn, n: int) -> float:
     graph.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / n
+    return per_step_us(a.elapsed_time(b), n)
 
 def event_us(fn, n: int):
     """Mean of per-call event intervals around n eager calls."""
@@ -223,6 +296,8 @@ def main(argv=None) -> int:
         return run_splitkv(args, dev, props)
     if args.workload == "fused-prefill":
         return run_fused_prefill(args, dev, props)
+    if args.workload == "read-ceiling":
+        return run_read_ceiling(args, dev, props)
     decode = args.workload == "decode"
     inp = {"decode": lambda: wl.llama_decode(args.history),
            "batching": wl.continuous_batching, "tiny": wl.tiny_fp32,
@@ -369,7 +444,8 @@ def main(argv=None) -> int:
             "batch": 1, "history": args.history, "kv_bytes_per_step": kv_bytes,
             "accumulate": "fp32",
             "cache": "MALL-warm (one pool)" if args.warm else
-                     f"cold: {copies} rotating pool copies, {copies * pool_bytes >> 20} MiB",
+                     f"cold: step i reads pool copy i mod {copies} ({copies * pool_bytes >> 20} "
+                     "MiB of copies); 512 MiB flush read before the timed replay",
             "blocks_per_split": plan.blocks_per_split, "splits": plan.max_splits,
             "grid": list(grid), "combine": "separate kernel" if comb else "in-launch",
         },
@@ -401,10 +477,11 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
-        best, sample = cpu_baseline(inp, args.cpu_seconds)
-        rec["cpu_baseline"] = {"value": round(kv_bytes / best / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle", "sample": sample,
-                               "ms_per_step": round(best * 1e3, 3)}
+        best, sample, threads = cpu_baseline(inp, args.cpu_seconds)
+        best1, _, _ = cpu_baseline(inp, min(3.0, args.cpu_seconds), threads=1)
+        rec["cpu_baseline"] = cpu_record(round(rate(kv_bytes, best * 1e6), 4), "GB/s", sample,
+                                         threads, ms_per_step=round(best * 1e3, 3),
+                                         one_thread_gbs=round(rate(kv_bytes, best1 * 1e6), 4))
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
@@ -457,10 +534,10 @@ def report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies) -
     }
     if not args.no_cpu_baseline:
         seqs = [0, 1, 2, 3]
-        best, sample = cpu_baseline(inp, args.cpu_seconds, seqs=seqs)
+        best, sample, threads = cpu_baseline(inp, args.cpu_seconds, seqs=seqs)
         sub_bytes = 2 * inp.num_kv_heads * inp.head_dim * 2 * int(inp.context_lens[seqs].sum())
-        rec["cpu_baseline"] = {"value": round(sub_bytes / best / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle", "sample": sample}
+        rec["cpu_baseline"] = cpu_record(round(rate(sub_bytes, best * 1e6), 4), "GB/s", sample,
+                                         threads)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
@@ -490,9 +567,8 @@ def report_small(args, inp, plan, grid, us_per_step, err, props, K, copies) -> i
         "device": props.name,
     }
     if not args.no_cpu_baseline:
-        best, sample = cpu_baseline(inp, args.cpu_seconds)
-        rec["cpu_baseline"] = {"value": round(best * 1e6, 2), "unit": "us/step", "cores": 1,
-                               "kind": "oracle", "sample": sample}
+        best, sample, threads = cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_record(round(best * 1e6, 2), "us/step", sample, threads)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
@@ -573,12 +649,11 @@ def run_prefill(args, dev, props) -> int:
         "device": props.name,
     }
     if not args.no_cpu_baseline:
-        best, sample = cpu_baseline(inp, args.cpu_seconds, seqs=[0], prefill=True)
+        best, sample, threads = cpu_baseline(inp, args.cpu_seconds, seqs=[0], prefill=True)
         sub = wl.PagedInputs(**{**inp.__dict__, "context_lens": inp.context_lens[:1],
                                 "q_start": inp.q_start[:2]})
-        rec["cpu_baseline"] = {"value": round(causal_flops(sub) / best / 1e12, 6),
-                               "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                               "sample": sample}
+        rec["cpu_baseline"] = cpu_record(round(rate(causal_flops(sub), best * 1e6, 1e12), 6),
+                                         "TFLOP/s", sample, threads)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
@@ -685,10 +760,10 @@ def run_splitkv(args, dev, props) -> int:
         "device": props.name,
     }
     if not args.no_cpu_baseline:
-        bst, sample = cpu_baseline(cpu_inp, args.cpu_seconds)
-        rec["cpu_baseline"] = {"value": round(cpu_inp.kv_bytes() / bst / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
-                               "sample": f"N={cpu_inp.context_lens[0].item()}: {sample}"}
+        bst, sample, threads = cpu_baseline(cpu_inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_record(round(rate(cpu_inp.kv_bytes(), bst * 1e6), 4), "GB/s",
+                                         f"N={cpu_inp.context_lens[0].item()}: {sample}",
+                                         threads)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
@@ -796,14 +871,70 @@ def run_fused_prefill(args, dev, props) -> int:
     }
     if not args.no_cpu_baseline:
         small = wl.fused_prefill(1024)
-        best, sample = cpu_baseline(small, args.cpu_seconds, seqs=[0], prefill=True)
+        best, sample, threads = cpu_baseline(small, args.cpu_seconds, seqs=[0], prefill=True)
         sub = wl.PagedInputs(**{**small.__dict__, "context_lens": small.context_lens[:1],
                                 "q_start": small.q_start[:2]})
-        rec["cpu_baseline"] = {"value": round(causal_flops(sub) / best / 1e12, 6),
-                               "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                               "sample": f"one 1024-token prompt: {sample}"}
+        rec["cpu_baseline"] = cpu_record(round(rate(causal_flops(sub), best * 1e6, 1e12), 6),
+                                         "TFLOP/s", f"one 1024-token prompt: {sample}", threads)
     else:
         rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+READ_CEILING_SHAPES = ([(w, 256, u) for w in (256, 512, 1024, 2048) for u in (1, 2, 4, 8, 16)] +
+                       [(256, t, u) for t in (512, 1024) for u in (1, 2, 4, 8, 16)])
+
+
+def run_read_ceiling(args, dev, props) -> int:
+    """Best single-launch time of a plain read of 8 MiB (the headline's K/V
+    bytes) over grid shapes and loads in flight, cold: step i reads copy
+    i mod 128 of 1 GiB, with the 512 MiB flush before the timed replay."""
+    import torch
+
+    from paged_kv_cache_178_amd import binding
+
+    nbytes = 8 << 20
+    copies = 128
+    buf = torch.ones((copies, nbytes), dtype=torch.uint8, device=dev)
+    sink = torch.empty(2048 * 1024, dtype=torch.int32, device=dev)
+    K = args.steps
+    empty_us = graph_us(lambda i: binding.np_probe_empty(), K)
+    log(f"[bench] empty kernel: {empty_us:.3f} us per graph step")
+    rows = []
+    for wgs, wg, u in READ_CEILING_SHAPES:
+        def step(i, wgs=wgs, wg=wg, u=u):
+            binding.np_probe_stream_read_ex(buf[i % copies], wgs, wg, u, sink)
+        us = graph_us(step, K)
+        per_thread = nbytes // 16 / (wgs * wg)
+        rows.append({"workgroups": wgs, "threads": wg, "loads_in_flight": u,
+                     "chunks_per_thread": per_thread, "us": round(us, 3),
+                     "gbs": round(rate(nbytes, us), 1)})
+        log(f"[bench] read {nbytes} B: {wgs} x {wg} threads, {u} loads in flight "
+            f"({per_thread:g} chunks per thread): {us:.3f} us, {rate(nbytes, us):.0f} GB/s")
+    best = min(rows, key=lambda r: r["us"])
+    by_grid = {}
+    for r in rows:
+        key = (r["workgroups"], r["threads"])
+        if key not in by_grid or r["us"] < by_grid[key]["us"]:
+            by_grid[key] = r
+    rec = {
+        "metric": "single-launch plain read of 8 MiB, GB/s (the decode step's read ceiling)",
+        "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": 0,
+        "ms_per_step": round(best["us"] / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "np_probe_stream_read_ex over 8 MiB, graph-timed, cold copies",
+                   "bytes": nbytes, "copies": copies},
+        "empty_kernel_us_graph": round(empty_us, 3),
+        "best": best,
+        "best_per_grid": list(by_grid.values()),
+        "sweep": rows,
+        "roofline": {"bound": "hbm", "achieved": best["gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(best["gbs"] / PEAK_HBM_GBS, 4),
+                     "traffic": None, "kernel": "probe_stream_read_kernel"},
+        "cpu_baseline": None,
+        "device": props.name,
+    }
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -891,18 +1022,12 @@ def run_append(args, dev, props) -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        import time
-
-        times = []
-        t_end = time.perf_counter() + args.cpu_seconds
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            oracle.append_kv(k_pool, v_pool, table, lens, new_start, k_new, v_new)
-            times.append(time.perf_counter() - t0)
-        best = min(times)
-        rec["cpu_baseline"] = {"value": round(traffic_alg / best / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
-                               "sample": f"full workload, best of {len(times)} runs"}
+        times = time_runs(lambda: oracle.append_kv(k_pool, v_pool, table, lens, new_start,
+                                                   k_new, v_new), args.cpu_seconds)
+        st = run_stats(times)
+        rec["cpu_baseline"] = cpu_record(
+            round(rate(traffic_alg, st["best"] * 1e6), 4), "GB/s",
+            f"full workload (numpy copies, one thread), best of {st['runs']} runs", 1)
     print(json.dumps(rec), flush=True)
     return 0
 

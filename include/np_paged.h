@@ -328,6 +328,13 @@ np_status np_paged_kv_append(const np_paged_desc* desc, const np_plan_t* plan,
 np_status np_probe_empty(void* stream);
 np_status np_probe_stream_read(const void* src, size_t bytes, uint32_t num_wgs, void* sink,
                                size_t sink_bytes, void* stream);
+/* The same read with wg_size threads per workgroup (a multiple of 64, at most
+ * 1024) and loads_per_thread (1, 2, 4, 8 or 16) 16-byte loads of a thread in
+ * flight at once; sink holds num_wgs * wg_size words. The single-launch read
+ * ceiling is the best time over these shapes. */
+np_status np_probe_stream_read_ex(const void* src, size_t bytes, uint32_t num_wgs,
+                                  uint32_t wg_size, uint32_t loads_per_thread, void* sink,
+                                  size_t sink_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* np_status_string(np_status status);

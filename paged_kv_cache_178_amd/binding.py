@@ -9,11 +9,11 @@ is no fallback path.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnp_paged.so")
+TRACE_LIB_PATH = os.path.join(PKG, "libnp_paged_trace.so")
 
 NP_F32, NP_F16, NP_BF16 = 0, 1, 2
 
@@ -57,6 +57,7 @@ class PlanOpts(ctypes.Structure):
 
 
 _LIB = None
+_TRACE_LIB = None
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
@@ -64,69 +65,90 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with paged_kv_cache_178_amd.build.build() "
-                "(there is no CPU fallback)")
-        lib = ctypes.CDLL(LIB_PATH)
-        lib.np_status_string.restype = ctypes.c_char_p
-        lib.np_status_string.argtypes = [ctypes.c_int]
-        lib.np_next_pow2.restype = ctypes.c_int32
-        lib.np_next_pow2.argtypes = [ctypes.c_int32]
-        lib.np_check_paged_inputs.restype = ctypes.c_int
-        lib.np_check_paged_inputs.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P,
-                                              _I32P, _I32P, _I32P]
-        lib.np_plan.restype = ctypes.c_int
-        lib.np_plan.argtypes = [ctypes.POINTER(Desc), _I32P, _I32P, ctypes.POINTER(PlanOpts),
-                                ctypes.POINTER(_P)]
-        lib.np_plan_destroy.restype = None
-        lib.np_plan_destroy.argtypes = [_P]
-        lib.np_plan_workspace_bytes.restype = ctypes.c_size_t
-        lib.np_plan_workspace_bytes.argtypes = [_P]
-        for name in ("np_plan_blocks_per_split", "np_plan_max_splits", "np_plan_is_prefill",
-                     "np_plan_schedule"):
-            getattr(lib, name).restype = ctypes.c_int32
-            getattr(lib, name).argtypes = [_P]
-        lib.np_plan_num_work_items.restype = ctypes.c_int64
-        lib.np_plan_num_work_items.argtypes = [_P]
-        lib.np_plan_work_item.restype = ctypes.c_int
-        lib.np_plan_work_item.argtypes = [_P, ctypes.c_int64, _I32P]
-        lib.np_plan_launch_shape.restype = ctypes.c_int
-        lib.np_plan_launch_shape.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32),
-                                             ctypes.POINTER(ctypes.c_uint32),
-                                             ctypes.POINTER(ctypes.c_uint32)]
-        lib.np_paged_attention_decode.restype = ctypes.c_int
-        lib.np_paged_attention_decode.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P,
-                                                  _P, _P, ctypes.c_size_t, _P]
-        lib.np_paged_attention_prefill.restype = ctypes.c_int
-        lib.np_paged_attention_prefill.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P,
-                                                   _P, _P, _P, _P, ctypes.c_size_t, _P]
-        lib.np_paged_kv_append.restype = ctypes.c_int
-        lib.np_paged_kv_append.argtypes = [ctypes.POINTER(Desc), _P, _P, _P,
-                                           ctypes.POINTER(ctypes.c_int64), _P, _P, _P, _P, _P,
-                                           _P]
-        lib.np_alloc_create.restype = ctypes.c_int
-        lib.np_alloc_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_int32, _I32P, ctypes.POINTER(_P)]
-        lib.np_alloc_destroy.restype = None
-        lib.np_alloc_destroy.argtypes = [_P]
-        lib.np_alloc_extend.restype = ctypes.c_int
-        lib.np_alloc_extend.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
-        lib.np_alloc_release.restype = ctypes.c_int
-        lib.np_alloc_release.argtypes = [_P, ctypes.c_int32]
-        lib.np_alloc_free_blocks.restype = ctypes.c_int32
-        lib.np_alloc_free_blocks.argtypes = [_P]
-        lib.np_alloc_block_table.restype = _I32P
-        lib.np_alloc_block_table.argtypes = [_P]
-        lib.np_alloc_context_lens.restype = _I32P
-        lib.np_alloc_context_lens.argtypes = [_P]
-        lib.np_probe_empty.restype = ctypes.c_int
-        lib.np_probe_empty.argtypes = [_P]
-        lib.np_probe_stream_read.restype = ctypes.c_int
-        lib.np_probe_stream_read.argtypes = [_P, ctypes.c_size_t, ctypes.c_uint32, _P,
-                                             ctypes.c_size_t, _P]
-        _LIB = lib
+        _LIB = _load(LIB_PATH)
     return _LIB
+
+
+def trace_library():
+    """The trace build (libnp_paged_trace.so: the same entry points plus
+    np_debug_set_trace); raises if it has not been built."""
+    global _TRACE_LIB
+    if _TRACE_LIB is None:
+        lib = _load(TRACE_LIB_PATH)
+        lib.np_debug_set_trace.restype = ctypes.c_int
+        lib.np_debug_set_trace.argtypes = [_P, ctypes.c_size_t]
+        _TRACE_LIB = lib
+    return _TRACE_LIB
+
+
+def _load(path):
+    """Load one build of the library and declare its C signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with paged_kv_cache_178_amd.build.build() "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    lib.np_status_string.restype = ctypes.c_char_p
+    lib.np_status_string.argtypes = [ctypes.c_int]
+    lib.np_next_pow2.restype = ctypes.c_int32
+    lib.np_next_pow2.argtypes = [ctypes.c_int32]
+    lib.np_check_paged_inputs.restype = ctypes.c_int
+    lib.np_check_paged_inputs.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P,
+                                          _I32P, _I32P, _I32P]
+    lib.np_plan.restype = ctypes.c_int
+    lib.np_plan.argtypes = [ctypes.POINTER(Desc), _I32P, _I32P, ctypes.POINTER(PlanOpts),
+                            ctypes.POINTER(_P)]
+    lib.np_plan_destroy.restype = None
+    lib.np_plan_destroy.argtypes = [_P]
+    lib.np_plan_workspace_bytes.restype = ctypes.c_size_t
+    lib.np_plan_workspace_bytes.argtypes = [_P]
+    for name in ("np_plan_blocks_per_split", "np_plan_max_splits", "np_plan_is_prefill",
+                 "np_plan_schedule"):
+        getattr(lib, name).restype = ctypes.c_int32
+        getattr(lib, name).argtypes = [_P]
+    lib.np_plan_num_work_items.restype = ctypes.c_int64
+    lib.np_plan_num_work_items.argtypes = [_P]
+    lib.np_plan_work_item.restype = ctypes.c_int
+    lib.np_plan_work_item.argtypes = [_P, ctypes.c_int64, _I32P]
+    lib.np_plan_launch_shape.restype = ctypes.c_int
+    lib.np_plan_launch_shape.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32),
+                                         ctypes.POINTER(ctypes.c_uint32),
+                                         ctypes.POINTER(ctypes.c_uint32)]
+    lib.np_paged_attention_decode.restype = ctypes.c_int
+    lib.np_paged_attention_decode.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P,
+                                              _P, _P, ctypes.c_size_t, _P]
+    lib.np_paged_attention_prefill.restype = ctypes.c_int
+    lib.np_paged_attention_prefill.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P,
+                                               _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.np_paged_kv_append.restype = ctypes.c_int
+    lib.np_paged_kv_append.argtypes = [ctypes.POINTER(Desc), _P, _P, _P,
+                                       ctypes.POINTER(ctypes.c_int64), _P, _P, _P, _P, _P,
+                                       _P]
+    lib.np_alloc_create.restype = ctypes.c_int
+    lib.np_alloc_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, _I32P, ctypes.POINTER(_P)]
+    lib.np_alloc_destroy.restype = None
+    lib.np_alloc_destroy.argtypes = [_P]
+    lib.np_alloc_extend.restype = ctypes.c_int
+    lib.np_alloc_extend.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
+    lib.np_alloc_release.restype = ctypes.c_int
+    lib.np_alloc_release.argtypes = [_P, ctypes.c_int32]
+    lib.np_alloc_free_blocks.restype = ctypes.c_int32
+    lib.np_alloc_free_blocks.argtypes = [_P]
+    lib.np_alloc_block_table.restype = _I32P
+    lib.np_alloc_block_table.argtypes = [_P]
+    lib.np_alloc_context_lens.restype = _I32P
+    lib.np_alloc_context_lens.argtypes = [_P]
+    lib.np_probe_empty.restype = ctypes.c_int
+    lib.np_probe_empty.argtypes = [_P]
+    lib.np_probe_stream_read.restype = ctypes.c_int
+    lib.np_probe_stream_read.argtypes = [_P, ctypes.c_size_t, ctypes.c_uint32, _P,
+                                         ctypes.c_size_t, _P]
+    lib.np_probe_stream_read_ex.restype = ctypes.c_int
+    lib.np_probe_stream_read_ex.argtypes = [_P, ctypes.c_size_t, ctypes.c_uint32,
+                                            ctypes.c_uint32, ctypes.c_uint32, _P,
+                                            ctypes.c_size_t, _P]
+    return lib
 
 
 def library():
@@ -216,43 +238,44 @@ def make_desc_contiguous(q, k_cache, out=None, n_q_total=None, scale=None,
 
 
 class Plan:
-    """Owns one np_plan_t."""
+    """Owns one np_plan_t (made, used and released by the same library)."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, lib=None):
         self.handle = ctypes.c_void_p(handle)
+        self.lib = lib if lib is not None else _lib()
 
     def __del__(self):
-        if getattr(self, "handle", None) is not None and self.handle.value and _LIB is not None:
-            _LIB.np_plan_destroy(self.handle)
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self.lib.np_plan_destroy(self.handle)
             self.handle = None
 
     @property
     def workspace_bytes(self) -> int:
-        return int(_lib().np_plan_workspace_bytes(self.handle))
+        return int(self.lib.np_plan_workspace_bytes(self.handle))
 
     @property
     def blocks_per_split(self) -> int:
-        return int(_lib().np_plan_blocks_per_split(self.handle))
+        return int(self.lib.np_plan_blocks_per_split(self.handle))
 
     @property
     def max_splits(self) -> int:
-        return int(_lib().np_plan_max_splits(self.handle))
+        return int(self.lib.np_plan_max_splits(self.handle))
 
     @property
     def schedule(self) -> int:
         """1: uniform splits, 2: stream-K, 0: prefill."""
-        return int(_lib().np_plan_schedule(self.handle))
+        return int(self.lib.np_plan_schedule(self.handle))
 
     @property
     def is_prefill(self) -> bool:
-        return bool(_lib().np_plan_is_prefill(self.handle))
+        return bool(self.lib.np_plan_is_prefill(self.handle))
 
     def work_items(self):
-        n = int(_lib().np_plan_num_work_items(self.handle))
+        n = int(self.lib.np_plan_num_work_items(self.handle))
         buf = (ctypes.c_int32 * 5)()
         items = []
         for i in range(n):
-            st = _lib().np_plan_work_item(self.handle, i, buf)
+            st = self.lib.np_plan_work_item(self.handle, i, buf)
             if st:
                 raise NPError(st, "np_plan_work_item")
             items.append(tuple(buf))
@@ -262,7 +285,8 @@ class Plan:
         grid = (ctypes.c_uint32 * 3)()
         wg = ctypes.c_uint32()
         comb = ctypes.c_uint32()
-        st = _lib().np_plan_launch_shape(self.handle, grid, ctypes.byref(wg), ctypes.byref(comb))
+        st = self.lib.np_plan_launch_shape(self.handle, grid, ctypes.byref(wg),
+                                           ctypes.byref(comb))
         if st:
             raise NPError(st, "np_plan_launch_shape")
         return tuple(grid), int(wg.value), int(comb.value)
@@ -291,16 +315,20 @@ def np_check_paged_inputs(desc: Desc, q, k_pool, v_pool, block_table, context_le
     return int(st)
 
 
-def np_plan(desc: Desc, context_lens_host, q_start_host=None, opts: PlanOpts | None = None) -> Plan:
+def np_plan(desc: Desc, context_lens_host, q_start_host=None, opts: PlanOpts | None = None,
+            lib=None) -> Plan:
+    """`lib`: the library to plan with (default the product library; pass
+    trace_library() for a plan launched through the trace build)."""
+    lib = lib if lib is not None else _lib()
     ln_p, ln_keep = _i32_host(context_lens_host)
     qs_p, qs_keep = _i32_host(q_start_host)
     h = ctypes.c_void_p()
-    st = _lib().np_plan(ctypes.byref(desc), ln_p, qs_p,
-                        ctypes.byref(opts) if opts is not None else None, ctypes.byref(h))
+    st = lib.np_plan(ctypes.byref(desc), ln_p, qs_p,
+                     ctypes.byref(opts) if opts is not None else None, ctypes.byref(h))
     del ln_keep, qs_keep
     if st:
         raise NPError(st, "np_plan")
-    return Plan(h.value)
+    return Plan(h.value, lib)
 
 
 def _stream(stream):
@@ -313,8 +341,9 @@ def _stream(stream):
 
 def np_paged_attention_decode(desc: Desc, plan: Plan, q, k_pool, v_pool, block_table,
                               context_lens, out, workspace=None, stream=None) -> None:
+    """Launch through the library that made `plan`."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib().np_paged_attention_decode(ctypes.byref(desc), plan.handle, _ptr(q),
+    st = plan.lib.np_paged_attention_decode(ctypes.byref(desc), plan.handle, _ptr(q),
                                           _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                           _ptr(context_lens), _ptr(out), _ptr(workspace),
                                           ws_bytes, _stream(stream))
@@ -466,5 +495,20 @@ def np_probe_stream_read(src, num_wgs: int, sink, stream=None) -> None:
         raise NPError(st, "np_probe_stream_read")
 
 
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)
+def np_probe_stream_read_ex(src, num_wgs: int, wg_size: int, loads_per_thread: int, sink,
+                            stream=None) -> None:
+    st = _lib().np_probe_stream_read_ex(_ptr(src), src.numel() * src.element_size(),
+                                        int(num_wgs), int(wg_size), int(loads_per_thread),
+                                        _ptr(sink), sink.numel() * sink.element_size(),
+                                        _stream(stream))
+    if st:
+        raise NPError(st, "np_probe_stream_read_ex")
+
+
+def set_trace(buf) -> None:
+    """Register a device int32 buffer with the trace build (None: off)."""
+    lib = trace_library()
+    st = lib.np_debug_set_trace(None if buf is None else _ptr(buf),
+                                0 if buf is None else buf.numel() * buf.element_size())
+    if st:
+        raise NPError(st, "np_debug_set_trace")

@@ -62,7 +62,38 @@ struct DecodeParams {
   int32_t num_seqs;
   int32_t sk_cost;   // stream-K: virtual units per segment
   float scale_log2;
+  int32_t* trace;    // trace build only (NP_TRACE): per-workgroup records
 };
+
+// ------------------------------------------------------------- trace build
+//
+// Compiled with NP_TRACE (the debugging and measurement library
+// libnp_paged_trace.so, never the product library), the decode kernels write
+// one record per workgroup into the buffer registered with
+// np_debug_set_trace: the uniform-split kernel its coordinates and the
+// s_memrealtime time of each phase, the stream-K kernel the pieces it read
+// and the partial slots it merged (layouts in np_trace.h). A stamp first
+// waits for every outstanding memory operation of the wave, so the trace
+// build's timing is that of a kernel without overlap across the stamped
+// points. Without NP_TRACE the hooks are empty.
+#ifdef NP_TRACE
+struct Stamps {
+  uint64_t t[kTraceStamps];
+  __device__ __forceinline__ Stamps() {
+#pragma unroll
+    for (int i = 0; i < kTraceStamps; ++i) t[i] = 0;
+  }
+  __device__ __forceinline__ void at(int i) {
+    __builtin_amdgcn_s_waitcnt(0);
+    t[i] = __builtin_amdgcn_s_memrealtime();
+  }
+};
+__device__ __forceinline__ int32_t trace_where() { return int32_t(__smid()); }
+#else
+struct Stamps {
+  __device__ __forceinline__ void at(int) {}
+};
+#endif
 
 // ------------------------------------------------------------ element types
 
@@ -154,6 +185,51 @@ __device__ __forceinline__ void unpack16<NP_F32>(const uint4& a, float* f) {
   f[1] = __uint_as_float(a.y);
   f[2] = __uint_as_float(a.z);
   f[3] = __uint_as_float(a.w);
+}
+
+// Output rows hold head_dim channels, a multiple of 8 (16-bit types) or 4
+// (fp32) by the 16-byte row rule the host checks, with rows and the base
+// 16-byte aligned: a chunk of 2 or 4 channels starting at an even (multiple
+// of 4) channel below head_dim is whole and aligned, so it is one store.
+template <int DT>
+__device__ __forceinline__ void store_out2(void* base, int64_t idx, float a, float b);
+template <>
+__device__ __forceinline__ void store_out2<NP_F32>(void* base, int64_t idx, float a, float b) {
+  *reinterpret_cast<float2*>(static_cast<float*>(base) + idx) = make_float2(a, b);
+}
+template <>
+__device__ __forceinline__ void store_out2<NP_F16>(void* base, int64_t idx, float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f2_t;
+  const f2_t v = {a, b};
+  *reinterpret_cast<f16x2_t*>(static_cast<_Float16*>(base) + idx) =
+      __builtin_convertvector(v, f16x2_t);
+}
+template <>
+__device__ __forceinline__ void store_out2<NP_BF16>(void* base, int64_t idx, float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f2_t;
+  const f2_t v = {a, b};
+  *reinterpret_cast<bf16x2_t*>(static_cast<__bf16*>(base) + idx) =
+      __builtin_convertvector(v, bf16x2_t);
+}
+template <int DT>
+__device__ __forceinline__ void store_out4(void* base, int64_t idx, float4 x) {
+  if constexpr (DT == NP_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = x;
+  } else {
+    // Two packed pairs, one 8-byte store.
+    typedef __attribute__((ext_vector_type(2))) float f2_t;
+    const f2_t lo = {x.x, x.y}, hi = {x.z, x.w};
+    uint2 w;
+    if constexpr (DT == NP_BF16) {
+      w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+      w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+      *reinterpret_cast<uint2*>(static_cast<__bf16*>(base) + idx) = w;
+    } else {
+      w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2_t));
+      w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2_t));
+      *reinterpret_cast<uint2*>(static_cast<_Float16*>(base) + idx) = w;
+    }
+  }
 }
 
 template <int DT>
@@ -270,7 +346,7 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
   constexpr int NW = kDecodeWaves;
   constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
   constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
-  constexpr int UB = CPL > 1 ? 8 : 16;
+  constexpr int UB = CPL > 1 ? 4 : 8;
   const int wave = threadIdx.x / kWaveSize;
   const int lane = threadIdx.x % kWaveSize;
 
@@ -291,17 +367,16 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
 #pragma unroll
       for (int ci = 0; ci < CPL; ++ci) {
         const int chunk = lane + ci * kWaveSize;
-        ml[u][ci] = make_float2(-INFINITY, 0.0f);
-        a0[u][ci] = make_float2(0.f, 0.f);
-        a1[u][ci] = make_float2(0.f, 0.f);
-        if (j < splits && chunk < NCH) {
-          const int h = (chunk * 4) / D_PAD;
-          const int c = (chunk * 4) % D_PAD;
-          const int64_t part = part_of(j, h);
-          ml[u][ci] = fetch2(p.ws_ml + 2 * part);
-          a0[u][ci] = fetch2(p.ws_acc + part * D_PAD + c);
-          a1[u][ci] = fetch2(p.ws_acc + part * D_PAD + c + 2);
-        }
+        // Every lane loads (a split past the last re-reads the last one and
+        // gets weight 0), so the batch is issued without branches.
+        const int cc = chunk < NCH ? chunk : NCH - 1;
+        const int h = (cc * 4) / D_PAD;
+        const int c = (cc * 4) % D_PAD;
+        const int64_t part = part_of(j < splits ? j : splits - 1, h);
+        ml[u][ci] = fetch2(p.ws_ml + 2 * part);
+        a0[u][ci] = fetch2(p.ws_acc + part * D_PAD + c);
+        a1[u][ci] = fetch2(p.ws_acc + part * D_PAD + c + 2);
+        if (j >= splits || chunk >= NCH) ml[u][ci].x = -INFINITY;
       }
     }
 #pragma unroll
@@ -355,11 +430,8 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
     const int h = (chunk * 4) / D_PAD;
     const int c = (chunk * 4) % D_PAD;
     const int64_t o = int64_t(s) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1 + c;
-    const float r = 1.0f / d;
-    if (c + 0 < p.head_dim) store_out<DT>(p.out, o + 0, n.x * r);
-    if (c + 1 < p.head_dim) store_out<DT>(p.out, o + 1, n.y * r);
-    if (c + 2 < p.head_dim) store_out<DT>(p.out, o + 2, n.z * r);
-    if (c + 3 < p.head_dim) store_out<DT>(p.out, o + 3, n.w * r);
+    const float r = __builtin_amdgcn_rcpf(d);
+    if (c < p.head_dim) store_out4<DT>(p.out, o, make_float4(n.x * r, n.y * r, n.z * r, n.w * r));
   }
 }
 
@@ -381,10 +453,12 @@ __device__ __forceinline__ float wave_max_rows(float x) {
 // P.V for one pair of slots (ja, jb) held by this lane, 16-bit types: the two
 // slots' V values of each channel are packed side by side (v_perm) and the
 // two weights are rounded to the input type, so one v_dot2 adds both slots'
-// contributions of a channel in fp32.
+// contributions of a channel in fp32. The softmax denominator l adds the
+// same rounded pair (a v_dot2 against (1, 1)), so numerator and denominator
+// use identical weights.
 template <int DT, int G, int VEC>
 __device__ __forceinline__ void pv_pair(const uint4& va, const uint4& vb, const float (*w)[G],
-                                        int ja, int jb, float (*acc)[VEC]) {
+                                        int ja, int jb, float (*acc)[VEC], float* l) {
   const uint32_t a[4] = {va.x, va.y, va.z, va.w};
   const uint32_t b[4] = {vb.x, vb.y, vb.z, vb.w};
   uint32_t pr[8];
@@ -399,12 +473,15 @@ __device__ __forceinline__ void pv_pair(const uint4& va, const uint4& vb, const 
     const f2_t ww = {w[ja][h], w[jb][h]};
     if constexpr (DT == NP_BF16) {
       const bf16x2_t wp = __builtin_convertvector(ww, bf16x2_t);
+      l[h] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l[h],
+                                             false);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         acc[h][c] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, pr[c]),
                                                     acc[h][c], false);
     } else {
       const f16x2_t wp = __builtin_convertvector(ww, f16x2_t);
+      l[h] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, 0x3c003c00u), l[h], false);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         acc[h][c] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), acc[h][c],
@@ -457,7 +534,7 @@ __device__ __forceinline__ void wave_accumulate(
     const DecodeParams& p, const TableRow& bt_row, const int L, const int b_first, const int nwb,
     const int64_t head_off, const int row, const uint4 (&qv)[G],
     int (&ph)[DecodeShape<DT, D_PAD, BS>::NG],
-    LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st) {
+    LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st, Stamps* stamps = nullptr) {
   using S = DecodeShape<DT, D_PAD, BS>;
   constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, TPL = S::TPL, NLB = S::NLB;
   constexpr int NG = S::NG;
@@ -515,7 +592,7 @@ __device__ __forceinline__ void wave_accumulate(
   #pragma unroll
           for (int h = 0; h < G; ++h) {
             w[j][h] = __builtin_amdgcn_exp2f(sc[i][j][h] - m[h]);   // 0 for masked slots
-            l[h] += w[j][h];
+            if constexpr (DT == NP_F32) l[h] += w[j][h];            // 16-bit: in pv_pair
           }
         uint4 vv[NLB];
   #pragma unroll
@@ -538,7 +615,8 @@ __device__ __forceinline__ void wave_accumulate(
           }
         } else {
   #pragma unroll
-          for (int j = 0; j < NLB; j += 2) pv_pair<DT, G, VEC>(vv[j], vv[j + 1], w, j, j + 1, acc);
+          for (int j = 0; j < NLB; j += 2)
+            pv_pair<DT, G, VEC>(vv[j], vv[j + 1], w, j, j + 1, acc, l);
         }
       }
   };
@@ -571,6 +649,7 @@ __device__ __forceinline__ void wave_accumulate(
   if (nwb > 0) load_group(0, ka, va);
   for (int g0 = 0; g0 < nwb; g0 += 2 * NG) {
     if (g0 + NG < nwb) load_group(g0 + NG, kb, vb);
+    if (stamps != nullptr && g0 == 0) stamps->at(2);
     compute_group(g0, ka, va);
     if (g0 + NG >= nwb) break;
     if (g0 + 2 * NG < nwb) load_group(g0 + 2 * NG, ka, va);
@@ -692,6 +771,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   const int split = blockIdx.x / p.hkv;
   const int s = blockIdx.y;
   const int b0 = split * p.bps;
+  Stamps stamps;
+  stamps.at(0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int lane = threadIdx.x % kWaveSize;
   const int row = lane / LPR;
@@ -731,7 +812,37 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   nb = nb < p.max_blocks ? nb : p.max_blocks;
   int splits = (nb + p.bps - 1) / p.bps;
   splits = splits < p.max_splits ? splits : p.max_splits;
+  stamps.at(1);
+#ifdef NP_TRACE
+  int32_t* trec = p.trace ? p.trace + (int64_t(blockIdx.y) * gridDim.x + blockIdx.x) *
+                                          NP_TRACE_UNIFORM_WORDS
+                          : nullptr;
+  int32_t tflags = 1, tticket = -1;
+  auto trace_write = [&]() {
+    stamps.at(8);
+    if (threadIdx.x != 0 || trec == nullptr) return;
+    trec[0] = tflags;
+    trec[1] = trace_where();
+    trec[2] = s;
+    trec[3] = kvh;
+    trec[4] = split;
+    trec[5] = b0;
+    trec[6] = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
+    trec[7] = tticket;
+    trec[8] = splits;
+    trec[9] = 0;
+    for (int i = 0; i < kTraceStamps; ++i) {
+      trec[10 + 2 * i] = int32_t(uint32_t(stamps.t[i]));
+      trec[11 + 2 * i] = int32_t(uint32_t(stamps.t[i] >> 32));
+    }
+  };
+  if (split >= splits) {
+    if (threadIdx.x == 0 && trec != nullptr) trec[0] = 1;
+    return;
+  }
+#else
   if (split >= splits) return;
+#endif
   const int b1 = (b0 + p.bps) < nb ? (b0 + p.bps) : nb;
   const int nwb = (b1 - b0 - wave + NW - 1) / NW;   // blocks of this wave (may be <= 0)
 
@@ -743,7 +854,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
   // instead; both are masked by selects below, never by multiplication.
   const int64_t head_off = int64_t(kvh) * p.kv_s2 + q_ch + int64_t(row) * p.kv_s1;
 
-  wave_accumulate<DT, D_PAD, G, BS>(p, bt_row, L, b0 + wave, nwb, head_off, row, qv, ph, st);
+  wave_accumulate<DT, D_PAD, G, BS>(p, bt_row, L, b0 + wave, nwb, head_off, row, qv, ph, st,
+                                    &stamps);
+  stamps.at(3);
 
   const bool direct = splits == 1;
   wg_combine<DT, D_PAD, G, BS, 1>(
@@ -751,16 +864,23 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
       [&](int h, int c, float t0, float t1, float mm, float ll) {
         const int hg = kvh * G + h;
         if (direct) {
-          const float r = 1.0f / ll;
+          const float r = __builtin_amdgcn_rcpf(ll);
           const int64_t oi = int64_t(s) * p.o_s0 + int64_t(hg) * p.o_s1 + c;
-          store_out<DT>(p.out, oi, t0 * r);
-          store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
+          store_out2<DT>(p.out, oi, t0 * r, t1 * r);
         } else {
           const int64_t part = (int64_t(s) * p.hq + hg) * p.max_splits + split;
           publish2(p.ws_acc + part * D_PAD + c, t0, t1);
           if (c == 0) publish2(p.ws_ml + 2 * part, mm, ll);
         }
       });
+  stamps.at(4);
+#ifdef NP_TRACE
+  if (direct) tflags |= 4;
+  if (!FUSED || direct) {
+    trace_write();
+    return;
+  }
+#endif
   if constexpr (FUSED) {
     if (direct) return;
     // Last-arriver merge: every thread waits until its partial stores are
@@ -772,18 +892,35 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     uint32_t* cnt = p.ws_cnt + int64_t(s * p.hkv + kvh) * kCounterStride;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    stamps.at(5);
     if (threadIdx.x == 0) {
       const uint32_t prev =
           __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = prev == uint32_t(splits - 1);
+#ifdef NP_TRACE
+      tticket = int32_t(prev);
+#endif
     }
     __syncthreads();
+    stamps.at(6);
+#ifdef NP_TRACE
+    if (!last) {
+      trace_write();
+      return;
+    }
+    tflags |= 2;
+#else
     if (!last) return;
+#endif
     merge_splits<DT, D_PAD, G>(p, s, kvh, splits, [&](int j, int h) {
       return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
     });
     if (threadIdx.x == 0)
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamps.at(7);
+#ifdef NP_TRACE
+    trace_write();
+#endif
   }
 }
 
@@ -868,11 +1005,9 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int h
       mx = m_new;
     }
     const int64_t o = int64_t(s) * p.o_s0 + int64_t(head0 + h) * p.o_s1 + c;
-    const float r = 1.0f / d;
-    if (c + 0 < p.head_dim) store_out<DT>(p.out, o + 0, acc.x * r);
-    if (c + 1 < p.head_dim) store_out<DT>(p.out, o + 1, acc.y * r);
-    if (c + 2 < p.head_dim) store_out<DT>(p.out, o + 2, acc.z * r);
-    if (c + 3 < p.head_dim) store_out<DT>(p.out, o + 3, acc.w * r);
+    const float r = __builtin_amdgcn_rcpf(d);
+    if (c < p.head_dim)
+      store_out4<DT>(p.out, o, make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r));
   }
 }
 
@@ -925,7 +1060,26 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
   const int C = (U + W - 1) / W;
   int u = w * C;
   const int u_end = U < u + C ? U : u + C;
+#ifdef NP_TRACE
+  int32_t* trec = p.trace ? p.trace + int64_t(blockIdx.x) * NP_TRACE_SK_WORDS : nullptr;
+  int32_t t_pieces = 0, t_overflow = 0;
+  auto trace_header = [&](int n_merges) {
+    if (threadIdx.x != 0 || trec == nullptr) return;
+    trec[0] = t_pieces < NP_TRACE_SK_PIECES ? t_pieces : NP_TRACE_SK_PIECES;
+    trec[1] = n_merges;
+    trec[2] = trace_where();
+    trec[3] = t_overflow;
+    trec[4] = U;
+    trec[5] = C;
+    trec[6] = trec[7] = 0;
+  };
+  if (u >= u_end) {
+    trace_header(0);
+    return;
+  }
+#else
   if (u >= u_end) return;
+#endif
   // The sequence whose segments hold unit u: the last s with sk_pre[s] <= u
   // (every sequence has at least n_hg * sk_cost >= 1 units).
   int s = 0;
@@ -946,7 +1100,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
   bool first_piece = true;
   while (u < u_end) {
     if (u >= pre(s + 1)) ++s;   // u never passes a segment end, so one step
-    const int L = p.lens[s];
+    const int L = ((ConstI32Ptr)p.lens)[s];   // scalar load (lengths are read-only)
     int nb = (L + BS - 1) / BS;
     nb = nb < p.max_blocks ? nb : p.max_blocks;
     nb = nb > 0 ? nb : 0;
@@ -1009,10 +1163,9 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
         p, wave, lane, row, ch0, st, !first_piece,
         [&](int h, int c, float t0, float t1, float mm, float ll) {
           if (direct) {
-            const float r = 1.0f / ll;
+            const float r = __builtin_amdgcn_rcpf(ll);
             const int64_t oi = int64_t(s) * p.o_s0 + int64_t(head0 + h) * p.o_s1 + c;
-            store_out<DT>(p.out, oi, t0 * r);
-            store_out<DT>(p.out, oi + 1, t1 * r);   // head_dim is even
+            store_out2<DT>(p.out, oi, t0 * r, t1 * r);
           } else {
             const int64_t part = int64_t(slot) * (HW * G) + h;
             publish2(p.ws_acc + part * D_PAD + c, t0, t1);
@@ -1020,6 +1173,21 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
           }
         });
     first_piece = false;
+#ifdef NP_TRACE
+    const bool t_keep = trec != nullptr && t_pieces < NP_TRACE_SK_PIECES;
+    int32_t* tp = t_keep ? trec + 8 + 8 * t_pieces : nullptr;
+    if (t_pieces >= NP_TRACE_SK_PIECES) t_overflow = 1;
+    if (threadIdx.x == 0 && t_keep) {
+      tp[0] = s;
+      tp[1] = hg;
+      tp[2] = b_lo;
+      tp[3] = b_hi;
+      tp[4] = direct ? -1 : slot;
+      tp[5] = n_pieces;
+      tp[6] = -1;
+      tp[7] = u;
+    }
+#endif
     if (!direct) {
       // Ticket, with the ordering of the split kernel's: stores complete,
       // then the ticket.
@@ -1030,6 +1198,9 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
         const uint32_t prev =
             __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sk_last = prev == uint32_t(n_pieces - 1);
+#ifdef NP_TRACE
+        if (t_keep) tp[6] = int32_t(prev);
+#endif
       }
       __syncthreads();
       if (__builtin_amdgcn_readfirstlane(sk_last)) {
@@ -1040,6 +1211,9 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
         mg_start[i] = seg_start;
       }
     }
+#ifdef NP_TRACE
+    ++t_pieces;
+#endif
     u = seg_end < u_end ? seg_end : u_end;
   }
   for (int i = 0; i < n_merge; ++i) {
@@ -1050,16 +1224,35 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
     const int wf = m0 / C;
     // Piece j belongs to workgroup wf + j; only the first can start inside
     // its workgroup's range.
-    merge_pieces<DT, D_PAD, HW * G>(p, ms, mh * HW * G, mn, [&](int j, int h) {
+    auto slot_of = [&](int j) {
       const int wj = wf + j;
       const int side = (j == 0 && m0 != wj * C) ? 1 : 0;
-      return int64_t(2 * wj + side) * (HW * G) + h;
+      return 2 * wj + side;
+    };
+#ifdef NP_TRACE
+    if (threadIdx.x == 0 && trec != nullptr) {
+      int32_t* tm = trec + NP_TRACE_SK_MERGE0 + NP_TRACE_SK_MERGE_WORDS * i;
+      tm[0] = ms;
+      tm[1] = mh;
+      tm[2] = mn;
+      tm[3] = m0;
+      tm[4] = wf;
+      tm[5] = tm[6] = tm[7] = 0;
+      for (int j = 0; j < mn && j < NP_TRACE_SK_SLOTS; ++j) tm[8 + j] = slot_of(j);
+      if (mn > NP_TRACE_SK_SLOTS) t_overflow = 1;
+    }
+#endif
+    merge_pieces<DT, D_PAD, HW * G>(p, ms, mh * HW * G, mn, [&](int j, int h) {
+      return int64_t(slot_of(j)) * (HW * G) + h;
     });
     // The next call that uses the counter is ordered after this launch.
     if (threadIdx.x == 0)
       __hip_atomic_store(p.ws_cnt + int64_t(ms * p.hkv + mh) * kCounterStride, 0u,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+#ifdef NP_TRACE
+  trace_header(n_merge);
+#endif
 }
 
 // Separate-launch merge of every (sequence, KV head) that was split.
@@ -1132,6 +1325,20 @@ np_status launch_decode_d(const DecodeParams& prm, const np_plan_core& c, hipStr
 
 using namespace np;
 
+#ifdef NP_TRACE
+namespace {
+void* g_trace = nullptr;
+size_t g_trace_bytes = 0;
+}  // namespace
+
+extern "C" np_status np_debug_set_trace(void* buf, size_t bytes) {
+  if (buf != nullptr && reinterpret_cast<uintptr_t>(buf) % 4 != 0) return NP_ERR_MISALIGNED;
+  g_trace = buf;
+  g_trace_bytes = buf ? bytes : 0;
+  return NP_OK;
+}
+#endif
+
 extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
                                                const np_plan_t* plan, const void* q,
                                                const void* k_pool, const void* v_pool,
@@ -1190,6 +1397,16 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
   prm.sk_cost = c.sk_cost;
   const float scale = desc->scale > 0.0f ? desc->scale : 1.0f / std::sqrt(float(c.head_dim));
   prm.scale_log2 = scale * kLog2e;
+  prm.trace = nullptr;
+#ifdef NP_TRACE
+  if (g_trace != nullptr) {
+    const size_t words = c.schedule == kScheduleStreamK ? NP_TRACE_SK_WORDS
+                                                        : NP_TRACE_UNIFORM_WORDS;
+    const size_t need = size_t(c.grid[0]) * c.grid[1] * c.grid[2] * words * sizeof(int32_t);
+    if (g_trace_bytes < need) return NP_ERR_WORKSPACE_TOO_SMALL;
+    prm.trace = static_cast<int32_t*>(g_trace);
+  }
+#endif
   hipStream_t hs = static_cast<hipStream_t>(stream);
   switch (c.dtype) {
     case NP_F32: return launch_decode_d<NP_F32>(prm, c, hs);

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "np_paged.h"
+#include "np_trace.h"
 
 namespace np {
 
@@ -26,6 +27,7 @@ constexpr int kSkMaxSeqs = 2048;               // stream-K: sequences per launch
 constexpr int kSkDefaultCost = 4;              // stream-K: virtual blocks per segment
 constexpr int kSkWgsPerCu = 2;                 // stream-K: resident decode workgroups per CU
 constexpr int kSkMinUnits = 8;                 // stream-K: least units per workgroup
+constexpr int kTraceStamps = NP_TRACE_STAMPS;  // trace build: phase stamps per workgroup
 
 // Stream-K: KV heads one decode workgroup serves (the largest of 4, 2, 1 that
 // divides Hkv).

@@ -22,13 +22,22 @@
 
 namespace np {
 
+// The table is never written during a launch, so its entries are read
+// through the constant address space: a wave-uniform entry then becomes a
+// scalar load (s_load, counted by lgkmcnt). A vector load of the same entry
+// would be counted by vmcnt, which retires in issue order, so waiting for the
+// next group's entries would also wait for every K/V load issued before them.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+
 struct TableRow {
   const int32_t* row;
   int32_t step;         // 1, or 0 for the contiguous layout (row[0] only)
   int32_t keep;         // -1 keeps the loaded entry, 0 drops it (contiguous)
   int32_t base;         // 0, or s * max_blocks_per_seq (contiguous)
   // The entry as loaded (the stand-in's first element when contiguous).
-  __device__ __forceinline__ int32_t raw(int b) const { return row[b * step]; }
+  __device__ __forceinline__ int32_t raw(int b) const {
+    return ((ConstI32Ptr)row)[b * step];
+  }
   // Physical block of logical block b from its raw entry: pure arithmetic,
   // no select, so the scalar load stays where a real table's load would be
   // and can be issued long before its use.
