@@ -243,6 +243,27 @@ np_status np_paged_attention_decode(const np_paged_desc* desc, const np_plan_t* 
                                     void* stream);
 
 /*
+ * np_paged_attention_decode_noalloc -- np_paged_attention_decode for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, checks,
+ * kernels and results, without the workspace: the workspace is a
+ * library-owned 8 MiB device array, one per GPU, held until the process
+ * ends. A plan whose np_plan_workspace_bytes exceeds 8 MiB returns
+ * NP_ERR_WORKSPACE_TOO_SMALL before anything is launched (the 64-sequence
+ * stream-K plan of the Llama head shape needs 4.3 MB). The first call on a
+ * device looks the array up and clears it with a fill kernel on `stream`;
+ * make that first call outside graph capture to keep the clear out of a
+ * captured graph. Every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU race: order them (one stream, or events).
+ * Allocates nothing and never synchronises.
+ */
+np_status np_paged_attention_decode_noalloc(const np_paged_desc* desc, const np_plan_t* plan,
+                                            const void* q, const void* k_pool,
+                                            const void* v_pool, const int32_t* block_table,
+                                            const int32_t* context_lens, void* out,
+                                            void* stream);
+
+/*
  * np_paged_attention_prefill -- a chunk of n_q_s new query rows per sequence,
  * causal: row i of sequence s sees keys t <= past_s + i ("Day 23", "What I
  * added today": past is computed on the host side of the interface; here the

@@ -117,6 +117,9 @@ def _load(path):
     lib.np_paged_attention_decode.restype = ctypes.c_int
     lib.np_paged_attention_decode.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P,
                                               _P, _P, ctypes.c_size_t, _P]
+    lib.np_paged_attention_decode_noalloc.restype = ctypes.c_int
+    lib.np_paged_attention_decode_noalloc.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P,
+                                                      _P, _P, _P]
     lib.np_paged_attention_prefill.restype = ctypes.c_int
     lib.np_paged_attention_prefill.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P,
                                                _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -349,6 +352,18 @@ def np_paged_attention_decode(desc: Desc, plan: Plan, q, k_pool, v_pool, block_t
                                           ws_bytes, _stream(stream))
     if st:
         raise NPError(st, "np_paged_attention_decode")
+
+
+def np_paged_attention_decode_noalloc(desc: Desc, plan: Plan, q, k_pool, v_pool, block_table,
+                                      context_lens, out, stream=None) -> None:
+    """The allocation-free decode: the library's per-device scratch array is
+    the workspace."""
+    st = plan.lib.np_paged_attention_decode_noalloc(ctypes.byref(desc), plan.handle, _ptr(q),
+                                                    _ptr(k_pool), _ptr(v_pool),
+                                                    _ptr(block_table), _ptr(context_lens),
+                                                    _ptr(out), _stream(stream))
+    if st:
+        raise NPError(st, "np_paged_attention_decode_noalloc")
 
 
 def np_paged_attention_prefill(desc: Desc, plan: Plan, q, k_pool, v_pool, block_table,

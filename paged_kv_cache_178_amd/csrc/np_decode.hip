@@ -33,6 +33,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "np_internal.h"
 #include "np_table.h"
@@ -1325,6 +1326,13 @@ np_status launch_decode_d(const DecodeParams& prm, const np_plan_core& c, hipStr
 
 using namespace np;
 
+namespace {
+np_status decode_call(const np_paged_desc* desc, const np_plan_t* plan, const void* q,
+                      const void* k_pool, const void* v_pool, const int32_t* block_table,
+                      const int32_t* context_lens, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+}  // namespace
+
 #ifdef NP_TRACE
 namespace {
 void* g_trace = nullptr;
@@ -1346,6 +1354,83 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
                                                const int32_t* context_lens, void* out,
                                                void* workspace, size_t workspace_bytes,
                                                void* stream) {
+  return decode_call(desc, plan, q, k_pool, v_pool, block_table, context_lens, out, workspace,
+                     workspace_bytes, stream);
+}
+
+namespace {
+
+// ------------------------------------------------- allocation-free variant
+//
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the decode workspace is this
+// file-scope device array instead of a caller buffer. Each GPU the library
+// runs on holds its own copy until the process ends. In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint4* p, size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += size_t(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The current device's scratch address; on a device's first call, looks it
+// up and clears the array on `stream` with a fill kernel (the arrival
+// counters at its start must begin at zero; every decode call leaves them
+// zero again).
+np_status scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return NP_ERR_HIP;
+    scratch_clear_kernel<<<dim3(1024), dim3(256), 0, stream>>>(static_cast<uint4*>(ptr),
+                                                               kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return NP_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return NP_OK;
+}
+
+}  // namespace
+
+extern "C" np_status np_paged_attention_decode_noalloc(const np_paged_desc* desc,
+                                                       const np_plan_t* plan, const void* q,
+                                                       const void* k_pool, const void* v_pool,
+                                                       const int32_t* block_table,
+                                                       const int32_t* context_lens, void* out,
+                                                       void* stream) {
+  np_status st = check_desc(desc);
+  if (st != NP_OK) return st;
+  st = check_pointers(desc, q, k_pool, v_pool, block_table, context_lens, out);
+  if (st != NP_OK) return st;
+  st = check_plan(desc, plan, 0);
+  if (st != NP_OK) return st;
+  if (plan->core.ws_bytes > kScratchBytes) return NP_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+  if (st != NP_OK) return st;
+  return decode_call(desc, plan, q, k_pool, v_pool, block_table, context_lens, out, ws,
+                     kScratchBytes, stream);
+}
+
+namespace {
+
+np_status decode_call(const np_paged_desc* desc, const np_plan_t* plan, const void* q,
+                      const void* k_pool, const void* v_pool, const int32_t* block_table,
+                      const int32_t* context_lens, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   np_status st = check_desc(desc);
   if (st != NP_OK) return st;
   st = check_pointers(desc, q, k_pool, v_pool, block_table, context_lens, out);
@@ -1415,3 +1500,5 @@ extern "C" np_status np_paged_attention_decode(const np_paged_desc* desc,
     default: return NP_ERR_BAD_DTYPE;
   }
 }
+
+}  // namespace
