@@ -39,9 +39,13 @@
  * library keeps no mutable global state; all calls are reentrant.
  *
  * Errors: every function returns an np_status; nothing throws or aborts
- * across this ABI. Device-side block-table entries and context lengths that
- * disagree with what the host validated are undefined behaviour (the kernels
- * clamp table reads to the table's width but not entry values to the pool).
+ * across this ABI. Device-side block-table entries that disagree with what
+ * the host validated are undefined behaviour (the kernels clamp table reads
+ * to the table's width but not entry values to the pool). Device-side
+ * lengths are read by the kernels: a device context length outside
+ * [1, max_blocks_per_seq * block_size], or one the plan's grid does not cover
+ * (see np_paged_attention_decode and _prefill), yields NaN in the affected
+ * outputs, never a silent truncation.
  */
 #ifndef NP_PAGED_H
 #define NP_PAGED_H
@@ -234,6 +238,13 @@ int32_t np_next_pow2(int32_t x);
  * Built kernels: block_size 16; head_dim a multiple of 8 (16-bit types) or 4
  * (fp32) up to 128; Hq/Hkv from 1 to 8. Other valid shapes return
  * NP_ERR_UNSUPPORTED.
+ * Device lengths: the stream-K schedule is recomputed on the device from
+ * context_lens, so any valid device length is attended in full. Under
+ * uniform splits the grid holds max_splits * blocks_per_split blocks per
+ * sequence, fixed by the host lengths the plan was made for: a sequence
+ * whose device length needs more (or is below 1 or above the table
+ * capacity) gets NaN in all its output heads, so a plan reused across steps
+ * must be remade once a length outgrows it.
  */
 np_status np_paged_attention_decode(const np_paged_desc* desc, const np_plan_t* plan,
                                     const void* q, const void* k_pool,
@@ -271,7 +282,10 @@ np_status np_paged_attention_decode_noalloc(const np_paged_desc* desc, const np_
  * QK^T and PV run on the MFMA units in bf16/fp16 with fp32 accumulation.
  * Built kernels: bf16 and fp16, head_dim 64, block_size 16, Hq/Hkv 1..8.
  * q_start is a device array [num_seqs + 1]. Same stream, allocation and
- * error rules as decode.
+ * error rules as decode. The grid covers the query rows of the host q_start
+ * the plan was made for (the longest chunk, in tiles): device rows beyond
+ * it, and every row of a sequence whose device length is below its row
+ * count or above the table capacity, are set to NaN.
  */
 np_status np_paged_attention_prefill(const np_paged_desc* desc, const np_plan_t* plan,
                                      const void* q, const void* k_pool,

@@ -248,6 +248,16 @@ __device__ __forceinline__ void store_out<NP_BF16>(void* base, int64_t idx, floa
   static_cast<__bf16*>(base)[idx] = static_cast<__bf16>(x);
 }
 
+// Heads h0 .. h0 + n - 1 of sequence s's output row set to NaN (the whole
+// workgroup takes part).
+template <int DT, typename Params>
+__device__ __forceinline__ void fill_nan(const Params& p, int s, int h0, int n) {
+  for (int i = threadIdx.x; i < n * p.head_dim; i += blockDim.x)
+    store_out<DT>(p.out, int64_t(s) * p.o_s0 + int64_t(h0 + i / p.head_dim) * p.o_s1 +
+                             i % p.head_dim,
+                  __builtin_nanf(""));
+}
+
 // ------------------------------------------------------- cross-lane helpers
 
 template <int CTRL>
@@ -810,9 +820,16 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 #pragma unroll
   for (int i = 0; i < NG; ++i) asm volatile("" ::"s"(ph[i]));
   int nb = (L + BS - 1) / BS;
-  nb = nb < p.max_blocks ? nb : p.max_blocks;
+  // A device length outside [1, table capacity], or longer than the grid of
+  // this plan covers (the plan was made for shorter host lengths), has no
+  // correct result here: the head group's outputs are set to NaN (by split
+  // 0, which every plan launches) instead of dropping the blocks past the
+  // last split.
+  if (L < 1 || L > p.max_blocks * BS || nb > p.max_splits * p.bps) {
+    if (split == 0) fill_nan<DT>(p, s, kvh * G, G);
+    return;
+  }
   int splits = (nb + p.bps - 1) / p.bps;
-  splits = splits < p.max_splits ? splits : p.max_splits;
   stamps.at(1);
 #ifdef NP_TRACE
   int32_t* trec = p.trace ? p.trace + (int64_t(blockIdx.y) * gridDim.x + blockIdx.x) *
@@ -1262,10 +1279,10 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams p
   const int kvh = blockIdx.x % p.hkv;
   const int s = blockIdx.x / p.hkv;
   const int L = p.lens[s];
-  int nb = (L + BS - 1) / BS;
-  nb = nb < p.max_blocks ? nb : p.max_blocks;
-  int splits = (nb + p.bps - 1) / p.bps;
-  splits = splits < p.max_splits ? splits : p.max_splits;
+  const int nb = (L + BS - 1) / BS;
+  // Lengths the decode kernel rejected (their outputs hold NaN) are left alone.
+  if (L < 1 || L > p.max_blocks * BS || nb > p.max_splits * p.bps) return;
+  const int splits = (nb + p.bps - 1) / p.bps;
   if (splits <= 1) return;
   merge_splits<DT, D_PAD, G>(p, s, kvh, splits, [&](int j, int h) {
     return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;

@@ -119,6 +119,26 @@ __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off) {
   return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
 }
 
+// Rows of units u0 .. units - 1 (unit u: query head kvh * G + u % G, rows
+// 64 (u / G) .. of the sequence's chunk) set to NaN, as raw bits (this file
+// is built without NaN semantics), 16 bytes per store; the whole workgroup
+// takes part.
+template <int DT>
+__device__ __forceinline__ void nan_units(const PrefillParams& p, int row0, int n_q, int kvh,
+                                          int G, int u0, int units) {
+  const uint32_t w = DT == NP_BF16 ? 0x7fc07fc0u : 0x7e007e00u;
+  const uint4 nan8 = make_uint4(w, w, w, w);
+  const int per_unit = kRows * (kD / 8);
+  for (int i = threadIdx.x; i < (units - u0) * per_unit; i += blockDim.x) {
+    const int u = u0 + i / per_unit;
+    const int r = (u / G) * kRows + (i % per_unit) / (kD / 8);
+    const int c = 8 * (i % (kD / 8));
+    if (r < n_q)
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + int64_t(row0 + r) * p.o_s0 +
+                                int64_t(kvh * G + u % G) * p.o_s1 + c) = nan8;
+  }
+}
+
 template <int DT, int BS>
 __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kernel(
     const PrefillParams p) {
@@ -146,7 +166,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   const int past = L - n_q;
   const int nqb = (n_q + kRows - 1) / kRows;
   const int units = G * nqb;
-  if (tile * NU >= units) return;
+  // Device rows or lengths that this plan's grid does not cover (a plan made
+  // for other host q_start or lengths), or that are invalid, get NaN rows
+  // from the first launched tile instead of being left unwritten.
+  const int plan_tiles = int(gridDim.x) / p.hkv;
+  const bool bad = past < 0 || L > p.max_blocks * BS;
+  const int first_uncovered = bad ? 0 : plan_tiles * NU;
+  if (tile == plan_tiles - 1 && units > first_uncovered)
+    nan_units<DT>(p, row0, n_q, kvh, G, first_uncovered, units);
+  if (bad || tile * NU >= units) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int grp = wave / NU;           // key tiles grp, grp + 2, grp + 4, ...

@@ -245,3 +245,40 @@ def test_strided_q_and_out():
     H.gpu_decode(inp, dev=dev, out=out)
     H.assert_close(out, H.oracle_out(inp), "f16", "strided")
     assert (out_wide[:, :2] == 7).all() and (out_wide[:, 10:] == 7).all()
+
+
+@pytest.mark.parametrize("combine_mode", [0, 1])
+def test_uniform_plan_shorter_than_device_lengths_gives_nan(combine_mode):
+    """A uniform-split plan made for shorter host lengths cannot cover a
+    longer device length: that sequence's outputs become NaN (never a silent
+    truncation); the sequences the plan covers stay correct, and the arrival
+    counters stay zero."""
+    inp = wl.custom(52, [4096, 300], hq=32, hkv=8, d=64, dtype="bf16")
+    dev = H.to_device(inp)
+    desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], scale=inp.scale)
+    plan = binding.np_plan(desc, np.array([1024, 300], np.int32), None,
+                           binding.PlanOpts(schedule=1, combine_mode=combine_mode))
+    assert plan.max_splits * plan.blocks_per_split < 4096 // 16
+    ws = binding.workspace_for(plan, "cuda")
+    out = torch.zeros_like(dev["q"])
+    binding.np_paged_attention_decode(desc, plan, dev["q"], dev["k_pool"], dev["v_pool"],
+                                      dev["block_table"], dev["context_lens"], out, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0].float()).all()
+    H.assert_close(out[1:], H.oracle_out(inp)[1:], "bf16", "covered sequence")
+    assert int(ws[: 256 * 2 * 8].view(torch.int32).abs().sum()) == 0
+
+
+def test_zero_device_length_gives_nan():
+    inp = wl.custom(53, [700, 64], hq=8, hkv=2, d=64, dtype="bf16")
+    dev = H.to_device(inp)
+    dev["context_lens"][1] = 0
+    desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], scale=inp.scale)
+    plan = binding.np_plan(desc, inp.context_lens, None, binding.PlanOpts(schedule=1))
+    ws = binding.workspace_for(plan, "cuda")
+    out = torch.zeros_like(dev["q"])
+    binding.np_paged_attention_decode(desc, plan, dev["q"], dev["k_pool"], dev["v_pool"],
+                                      dev["block_table"], dev["context_lens"], out, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all()
+    H.assert_close(out[:1], H.oracle_out(inp)[:1], "bf16", "valid sequence")

@@ -75,3 +75,28 @@ def test_equal_scores_give_causal_mean():
     inp = wl.custom(73, [600, 77], n_q=[90, 77], hq=8, hkv=4, d=64, dtype="f16")
     inp.q.zero_()
     _run(inp)
+
+
+def test_rows_beyond_the_plan_grid_give_nan():
+    """The prefill grid comes from the host q_start the plan was made with;
+    device rows past it (here 300 rows of sequence 0 on a plan for 200)
+    become NaN instead of staying unwritten, and the covered rows are
+    correct."""
+    import numpy as np
+
+    from paged_kv_cache_178_amd import binding
+
+    inp = wl.custom(54, [1300, 600], n_q=[300, 100], hq=8, hkv=2, d=64, dtype="bf16")
+    dev = H.to_device(inp)
+    out = torch.zeros_like(dev["q"])
+    desc = binding.make_desc(dev["q"], dev["k_pool"], dev["block_table"], out=out,
+                             scale=inp.scale)
+    plan = binding.np_plan(desc, inp.context_lens, np.array([0, 200, 400], np.int32))
+    binding.np_paged_attention_prefill(desc, plan, dev["q"], dev["k_pool"], dev["v_pool"],
+                                       dev["block_table"], dev["context_lens"], dev["q_start"],
+                                       out)
+    torch.cuda.synchronize()
+    ref = H.oracle_out(inp, prefill=True)
+    assert torch.isnan(out[256:300].float()).all()
+    H.assert_close(out[:256], ref[:256], "bf16", "covered rows of sequence 0")
+    H.assert_close(out[300:], ref[300:], "bf16", "sequence 1")
