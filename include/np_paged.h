@@ -139,6 +139,11 @@ typedef struct np_plan_s np_plan_t;   /* opaque, host memory only */
 /*
  * np_check_paged_inputs -- validate a call without touching the GPU.
  *
+ * ("Day 23: the real triton.jit paged-attention kernel", section "What I
+ * added today": every integer the kernels turn into a pointer or a bound is
+ * checked by host code that runs without a GPU; the shapes checked are the
+ * problem statement of "3. Paged KV-cache attention" in "I Wrote the Three
+ * Attention Kernels That Run LLM Inference".)
  * Checks the descriptor, the device pointers (non-NULL, 16-byte aligned for
  * q/pools/out, 4-byte for int32 arrays; block_table may be NULL, see
  * "Contiguous caches"), strides and GQA divisibility. When
@@ -224,6 +229,12 @@ int32_t np_next_pow2(int32_t x);
 /*
  * np_paged_attention_decode -- one query token per sequence.
  *
+ * (The fused paged read of "3. Paged KV-cache attention" -- each sequence's
+ * K/V found block by block through its table row, GQA-aware -- with the KV
+ * range of a sequence split across workgroups and merged by the log-sum-exp
+ * rule of "2. Split-KV flash-decoding", both in "I Wrote the Three Attention
+ * Kernels That Run LLM Inference"; the attention itself as defined in "What
+ * is attention, really?" of the same page.)
  * q/out [num_seqs, Hq, d]. Launches the split-KV decode kernel and, when any
  * sequence has more than one split, the combine kernel, asynchronously on
  * `stream` (a hipStream_t; NULL = the null stream). Never allocates, never

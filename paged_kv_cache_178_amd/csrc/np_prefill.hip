@@ -10,15 +10,20 @@
 // with K_s[t], V_s[t] read through the block table, KV head h / G.
 //
 // Decomposition:
-// * One 256-thread workgroup (4 wave64) per (sequence, KV head, tile). A tile
-//   is 4 units; a unit is one query head of the GQA group times 32 query rows
+// * One 512-thread workgroup (8 wave64) per (sequence, KV head, tile). A tile
+//   is 4 units; a unit is one query head of the GQA group times 64 query rows
 //   (units numbered head-fastest), so the waves of a workgroup share every
 //   K/V tile they stage: for G = 4 the four heads of the group.
-// * Key tiles of 64 keys (4 blocks of 16) are staged in LDS, double buffered:
-//   K as [key][channel] rows, V transposed to [channel][key]. Wave w loads
-//   block w of the tile (one table entry per wave).
-// * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = the wave's
-//   32 query rows held in registers), so each lane holds one query's scores:
+// * Each unit has two waves, one in each of two wave groups; group g takes key
+//   tiles g, g + 2, g + 4, ..., and at the end group 1 hands its (m, l, acc)
+//   to group 0 through LDS for the split-KV log-sum-exp merge. A wave holds
+//   its 64 query rows as two 32-column MFMA blocks, so every K and V^T
+//   operand read from LDS feeds two MFMAs.
+// * Key tiles of 64 keys (4 blocks of 16) are staged in LDS, double buffered,
+//   one tile per group per step: K as [key][channel] rows, V transposed to
+//   [channel][key]. Wave w stages block w % 4 of its group's tile.
+// * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = 32 of the
+//   wave's query rows held in registers), so each lane holds one query's scores:
 //   the online-softmax max and sum ("1. Fused prefill attention": stream K/V,
 //   reduce online, never materialise N x N) stay in the lane, plus one
 //   exchange with the lane 32 away.

@@ -514,3 +514,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         B.library()
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         B.np_plan(desc(), np.array([3, 5], np.int32))
+
+
+def test_contiguous_descriptor_strides():
+    """make_desc_contiguous on a dense [num_seqs, capacity, Hkv, d] cache: the
+    identity block mapping (block j of sequence s is physical block
+    s * max_blocks + j) with the derived strides addresses exactly the dense
+    tensor's element of every (sequence, token, head, channel)."""
+    import torch
+
+    ns, cap, hkv, d, bs = 3, 64, 2, 16, 16
+    k = torch.zeros(ns, cap, hkv, d, dtype=torch.bfloat16)
+    q = torch.zeros(ns, 4, d, dtype=torch.bfloat16)
+    dd = B.make_desc_contiguous(q, k, block_size=bs)
+    assert (dd.max_blocks_per_seq, dd.n_blocks, dd.block_size) == (cap // bs, ns * cap // bs, bs)
+    assert tuple(dd.kv_stride) == (bs * k.stride(1), k.stride(1), k.stride(2))
+    assert dd.bt_stride == dd.max_blocks_per_seq
+    for s in range(ns):
+        for t in range(cap):
+            for h in range(hkv):
+                blk = s * dd.max_blocks_per_seq + t // bs
+                off = blk * dd.kv_stride[0] + (t % bs) * dd.kv_stride[1] + h * dd.kv_stride[2]
+                assert off == s * k.stride(0) + t * k.stride(1) + h * k.stride(2)
+    assert check(dd, ptrs=dict(bt=None)) == S["NP_OK"]
+    with pytest.raises(ValueError):
+        B.make_desc_contiguous(q, torch.zeros(ns, 40, hkv, d, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        B.make_desc_contiguous(q, k[:, :, :, :].transpose(0, 1).contiguous().transpose(0, 1))
