@@ -353,7 +353,7 @@ __device__ __forceinline__ float2 fetch2(const float* p) {
 // in flight before any is used; the per-wave states are merged through LDS.
 template <int DT, int D_PAD, int G, typename PartOf>
 __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh, int splits,
-                                             PartOf&& part_of) {
+                                             PartOf&& part_of, bool write = true) {
   constexpr int NW = kDecodeWaves;
   constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
   constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
@@ -442,7 +442,8 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
     const int c = (chunk * 4) % D_PAD;
     const int64_t o = int64_t(s) * p.o_s0 + int64_t(kvh * G + h) * p.o_s1 + c;
     const float r = __builtin_amdgcn_rcpf(d);
-    if (c < p.head_dim) store_out4<DT>(p.out, o, make_float4(n.x * r, n.y * r, n.z * r, n.w * r));
+    if (write && c < p.head_dim)
+      store_out4<DT>(p.out, o, make_float4(n.x * r, n.y * r, n.z * r, n.w * r));
   }
 }
 
@@ -921,18 +922,25 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     }
     __syncthreads();
     stamps.at(6);
+    // Every workgroup runs the merge code, the others on a one-split dummy
+    // that stores nothing. There is one call site, so one copy of the code:
+    // the merging workgroup is the only one of its (sequence, KV head) on its
+    // XCC that needs it, and its instruction fetches then find the lines in
+    // the XCC's L2 instead of memory (measured: 0.2 us of the 4096-token
+    // step).
+    const bool is_last = last;
+    merge_splits<DT, D_PAD, G>(p, s, kvh, is_last ? splits : 1, [&](int j, int h) {
+      return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
+    }, is_last);
 #ifdef NP_TRACE
-    if (!last) {
+    if (!is_last) {
       trace_write();
       return;
     }
     tflags |= 2;
 #else
-    if (!last) return;
+    if (!is_last) return;
 #endif
-    merge_splits<DT, D_PAD, G>(p, s, kvh, splits, [&](int j, int h) {
-      return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
-    });
     if (threadIdx.x == 0)
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     stamps.at(7);
