@@ -423,7 +423,10 @@ def main(argv=None) -> int:
     # The timed region is K back-to-back launches of the decode kernel (one
     # kernel per step), so its average launch duration is the graph time / K.
     achieved = gbs
-    traffic = stored_traffic()
+    # The committed counter summary covers the default plan at 4096 tokens only.
+    default_plan = (args.history == 4096 and args.blocks_per_split == 0 and
+                    args.combine_mode == 0 and args.schedule == 0 and args.wgs_per_cu == 0)
+    traffic = stored_traffic() if default_plan and not args.warm else None
     rec = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -502,7 +505,9 @@ def report_batching(args, inp, plan, grid, us_per_step, err, props, K, copies) -
     kv_bytes = inp.kv_bytes()
     if args.workload in SMALL_DECODE:
         return report_small(args, inp, plan, grid, us_per_step, err, props, K, copies)
-    traffic = stored_traffic(PMC_SUMMARY_BATCHING)
+    # The committed counter summary covers the default stream-K plan only.
+    default_plan = (plan.schedule == 2 and args.segment_cost == 0 and args.wgs_per_cu == 0)
+    traffic = stored_traffic(PMC_SUMMARY_BATCHING) if default_plan else None
     gbs = kv_bytes / (us_per_step * 1e-6) / 1e9
     rec = {
         "metric": "paged-decode KV GB/s (% HBM peak), continuous batching",
