@@ -19,9 +19,12 @@
 //   to group 0 through LDS for the split-KV log-sum-exp merge. A wave holds
 //   its 64 query rows as two 32-column MFMA blocks, so every K and V^T
 //   operand read from LDS feeds two MFMAs.
-// * Key tiles of 64 keys (4 blocks of 16) are staged in LDS, double buffered,
-//   one tile per group per step: K as [key][channel] rows, V transposed to
-//   [channel][key]. Wave w stages block w % 4 of its group's tile.
+// * Key tiles of 64 keys (4 blocks of 16) are staged in LDS in three buffers
+//   per group, one tile per group per step, loaded two steps ahead straight
+//   from global memory into LDS (no register staging): K and V both as
+//   [key][channel] rows. Wave w loads block w % 4 of its group's tile. The
+//   workgroup copies its sequence's table row to LDS once, so a step finds its
+//   block without a scalar load from global memory.
 // * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = 32 of the
 //   wave's query rows held in registers), so each lane holds one query's scores:
 //   the online-softmax max and sum ("1. Fused prefill attention": stream K/V,
@@ -29,8 +32,8 @@
 //   exchange with the lane 32 away.
 // * O^T += V^T P^T on the same MFMA: P^T stays in the registers it was
 //   computed in (rounded to the input type); the keys of each k-step are taken
-//   in the order those registers hold them and V^T is read from LDS in the
-//   same order.
+//   in the order those registers hold them, and the V^T operand is read in the
+//   same order from the [key][channel] rows by a transposing LDS read.
 // * Scores are in log2 units (scale * log2 e folded in); exp2 is v_exp_f32.
 
 #include <hip/hip_runtime.h>
@@ -49,8 +52,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;       // log2 units: weights stay below 256
 constexpr int kKT = 64;             // keys per staged tile
 constexpr int kD = 64;              // head_dim handled by this kernel
-constexpr int kKRow = kD + 8;       // K row pitch in LDS (elements): 144 bytes
-constexpr int kVRow = kKT + 4;      // V^T row pitch in LDS (elements): 136 bytes
+constexpr int kStages = 3;         // LDS tile buffers per wave group (loads run 2 steps ahead)
+// Table entries a workgroup copies to LDS (longer histories read the rest
+// from the table in global memory).
+constexpr int kTabCache = 1024;
+
+// K and V tiles sit in LDS as [key][channel] rows of 128 bytes, written straight
+// from global memory (global_load_lds: lane l's 16 bytes land at base + 16 l)
+// with the 16-byte chunks of each row permuted by an XOR swizzle, so that each
+// 256-byte pass of an operand read touches every one of the 64 four-byte LDS
+// banks once (two key rows share one span of the banks, the even key's row
+// first):
+// * K (MFMA A operand of S^T, 16-byte reads): a pass reads chunk c of 16
+//   consecutive keys; slot c ^ ((key >> 1) & 7) gives the 8 even keys 8
+//   distinct slots, and the 8 odd keys likewise.
+// * V (ds_read_b64_tr_b16, 8-byte transposing reads): a pass reads chunks
+//   c .. c + 3 of 4 consecutive keys; slot c ^ (((key >> 1) & 1) << 2) moves
+//   keys 2 and 3 of each 4 to the other half of their rows.
+__device__ __forceinline__ int k_slot(int key, int chunk) { return chunk ^ ((key >> 1) & 7); }
+__device__ __forceinline__ int v_slot(int key, int chunk) { return chunk ^ (((key >> 1) & 1) << 2); }
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 constexpr int kRows = kPrefillRowsPerWave;   // query rows per unit (two MFMA column blocks)
 
 struct PrefillParams {
@@ -153,10 +176,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   static_assert(NG == 2 && NU * BS == kKT, "two groups; one block per wave per tile");
   constexpr int QB = kRows / 32;          // 32-query column blocks per wave
   static_assert(QB == 2, "the step below pairs two query blocks");
-  // Double-buffered pairs of key tiles (tile 2j + g is group g's in step j).
-  constexpr int kKTile = kKT * kKRow, kVTile = kD * kVRow;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][NG][kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][NG][kVTile];
+  // kStages buffers per group of K and V tiles (tile 2j + g is group g's in
+  // step j, in buffer j % kStages).
+  constexpr int kTile = kKT * kD;
+  // One LDS variable for all staged tiles (K stages, then V stages) and the
+  // copy of the first kTabCache raw entries of the sequence's table row. (With
+  // separate variables the compiler tags each access with its variable alone,
+  // and would no longer see that a step's loads and reads use different
+  // buffers of the same array.)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStages * NG * kTile + 2 * kTabCache];
+  auto& k_lds = *reinterpret_cast<uint16_t(*)[kStages][NG][kTile]>(lds);
+  auto& v_lds = *reinterpret_cast<uint16_t(*)[kStages][NG][kTile]>(lds + kStages * NG * kTile);
+  int32_t* const tab = reinterpret_cast<int32_t*>(lds + 2 * kStages * NG * kTile);
 
   const int kvh = blockIdx.x % p.hkv;
   // Tiles are launched largest first: later query rows see more keys under the
@@ -220,51 +251,57 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
       qreg[qb][c] = q_ok[qb] ? ld16(p.q, qoff + 16 * c) : make_uint4(0, 0, 0, 0);
   }
 
-  // Staging map: in step j, wave w stages block w % NU of tile 2j + w / NU;
-  // lane (kp, cc) holds slots 2kp, 2kp+1 of that block, channels 8cc .. 8cc+7.
-  const int kp = lane / 8;
-  const int cc = lane % 8;
+  // Staging: in step j, wave w loads block w % NU of its group's tile 2j + w / NU
+  // (16 keys, rows 16 (w % NU) ..) of K and of V straight into the tile
+  // buffers, 8 rows per instruction; lane l fetches the chunk its LDS slot
+  // holds under the swizzle. Blocks past the history re-read the last real
+  // block; their rows, and the slots past the history in the last block, are
+  // zeroed in V after the loads land (keys there get weight 0, and 0 times an
+  // unwritten slot must not turn into NaN). K rows there are masked by score
+  // selects.
   const TableRow bt_row = table_row(p.bt, p.bt_stride, s, p.max_blocks, p.bt_contig);
   int nb = (L + BS - 1) / BS;
   nb = nb < p.max_blocks ? nb : p.max_blocks;
-  uint4 kst[2], vst[2];
-  // Loads are unconditional: a block past the history (or a tile past the
-  // last) reads the last real block instead, and what it stages is never used
-  // unmasked.
-  auto stage_load = [&](int j) {
-    int blk = (NG * j + grp) * NU + wu;
-    blk = blk < nb ? blk : nb - 1;
-    const int64_t base = int64_t(bt_row[blk]) * p.kv_s0 + int64_t(kvh) * p.kv_s2 + 8 * cc +
-                         int64_t(2 * kp) * p.kv_s1;
-    kst[0] = ld16(p.k, base);
-    kst[1] = ld16(p.k, base + p.kv_s1);
-    vst[0] = ld16(p.v, base);
-    vst[1] = ld16(p.v, base + p.kv_s1);
-  };
-  auto stage_store = [&](int j) {
+  // Logical block wave (grp, wu) stages in step j (past the history: the last one).
+  auto block_of = [&](int j) __attribute__((always_inline)) {
     const int blk = (NG * j + grp) * NU + wu;
-    uint16_t* kl = k_lds[j % 2][grp];
-    uint16_t* vl = vt_lds[j % 2][grp];
-    const int key0 = wu * BS + 2 * kp;              // key index within the tile
-    const int t0 = blk * BS + 2 * kp;               // absolute key of slot 2kp
-    // V rows of keys past the history are zero (their weight is 0 and 0 * V
-    // must not turn into NaN); K rows there are masked by score selects.
-    const bool ok0 = blk < nb && t0 < L;
-    const bool ok1 = blk < nb && t0 + 1 < L;
-    *reinterpret_cast<uint4*>(&kl[key0 * kKRow + 8 * cc]) = kst[0];
-    *reinterpret_cast<uint4*>(&kl[(key0 + 1) * kKRow + 8 * cc]) = kst[1];
-    const uint32_t a[4] = {ok0 ? vst[0].x : 0u, ok0 ? vst[0].y : 0u, ok0 ? vst[0].z : 0u,
-                           ok0 ? vst[0].w : 0u};
-    const uint32_t b[4] = {ok1 ? vst[1].x : 0u, ok1 ? vst[1].y : 0u, ok1 ? vst[1].z : 0u,
-                           ok1 ? vst[1].w : 0u};
+    return blk < nb ? blk : nb - 1;
+  };
+  auto stage_issue = [&](int phys, const uint16_t* ksrc, const uint16_t* vsrc, uint16_t* kdst,
+                         uint16_t* vdst) __attribute__((always_inline)) {
+    const int64_t base = int64_t(phys) * p.kv_s0 + int64_t(kvh) * p.kv_s2;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      // channel 8cc + 2jj: low halves; channel 8cc + 2jj + 1: high halves.
-      *reinterpret_cast<uint32_t*>(&vl[(8 * cc + 2 * jj) * kVRow + key0]) =
-          __builtin_amdgcn_perm(b[jj], a[jj], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(&vl[(8 * cc + 2 * jj + 1) * kVRow + key0]) =
-          __builtin_amdgcn_perm(b[jj], a[jj], 0x07060302u);
+    for (int n = 0; n < 2; ++n) {
+      const int slot_row = 8 * n + lane / 8;       // slot of the block, row 16 wu + slot_row
+      const int key = BS * wu + slot_row;          // row of the tile
+      const int64_t src = base + int64_t(slot_row) * p.kv_s1;
+      const int off = (BS * wu + 8 * n) * kD;      // wave-uniform destination row
+      __builtin_amdgcn_global_load_lds(
+          ksrc + src + 8 * k_slot(key, lane % 8),
+          (LdsPtr)(kdst + off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          vsrc + src + 8 * v_slot(key, lane % 8),
+          (LdsPtr)(vdst + off), 16, 0, 0);
     }
+  };
+  auto stage_fix = [&](int j, uint16_t* vl) __attribute__((always_inline)) {
+    const int key0 = ((NG * j + grp) * NU + wu) * BS;   // first key of the (unclamped) block
+    if (key0 + BS <= L) return;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int slot_row = 8 * n + lane / 8;
+      if (key0 + slot_row >= L)
+        *reinterpret_cast<uint4*>(&vl[(BS * wu + slot_row) * kD + 8 * (lane % 8)]) =
+            make_uint4(0, 0, 0, 0);
+    }
+  };
+  // Wait until at most four (the next stage's) or none of this wave's loads
+  // are outstanding (only the staging loads are in flight in the loop).
+  auto wait_loads = [&](bool pending4) __attribute__((always_inline)) {
+    if (pending4)
+      __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): the next stage's loads may fly on
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
 
   const float c = p.scale_log2;
@@ -284,7 +321,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   // more than kLazy, decided for the whole wave by a ballot, so the
   // cross-lane exchange and the rescale of acc are rare. Weights stay below
   // 2^kLazy, well inside the input type's range.
-  auto softmax_head = [&](int kt, int qb, f32x16_t (&st)[2]) {
+  auto softmax_head = [&](int kt, int qb, f32x16_t (&st)[2]) __attribute__((always_inline)) {
     const int key_base = kt * kKT;
     const bool need_mask = key_base + kKT - 1 > past + q0 + 32 * qb || key_base + kKT > L;
     if (need_mask) {
@@ -320,7 +357,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   // A lane whose scores so far were all masked still has m = -inf (a wave
   // group may start on a tile that some of its rows cannot see): its weights
   // must be 0, not exp2(-inf + inf).
-  auto weights = [&](int qb, int ks, const f32x16_t (&st)[2], uint4 (&pb)[4]) {
+  auto weights = [&](int qb, int ks, const f32x16_t (&st)[2], uint4 (&pb)[4]) __attribute__((always_inline)) {
     const float neg_m = m[qb] == -INFINITY ? 0.0f : -m[qb];
     float e[8];
 #pragma unroll
@@ -344,13 +381,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   //   P.V of block 1
   // Register j of k-step ks of P^T holds key 16 ks + 8 (j / 4) + 4 half + j % 4
   // of the tile; V^T is read in that order.
-  auto tile_step = [&](int kt, const uint16_t* kl, const uint16_t* vl) {
+  auto tile_step = [&](int kt, const uint16_t* kl, const uint16_t* vl) __attribute__((always_inline)) {
     uint4 ka[2][kD / 16];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int k = 0; k < kD / 16; ++k)
-        ka[b][k] = *reinterpret_cast<const uint4*>(&kl[(32 * b + col) * kKRow + 16 * k + 8 * half]);
+      for (int k = 0; k < kD / 16; ++k) {
+        const int key = 32 * b + col;
+        ka[b][k] = *reinterpret_cast<const uint4*>(&kl[key * kD + 8 * k_slot(key, 2 * k + half)]);
+      }
     f32x16_t s0[2], s1[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -370,15 +409,31 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
       weights(0, ks, s0, pb0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // V^T operand (A of O^T = V^T P^T): lane l needs keys 16 ks + 4 half + 0..3
+    // and + 8 .. + 11 of channel 32 cb + l % 32. A transposing read hands lane t
+    // of a 16-lane group element t % 4 of the 4-element vector addressed by lane
+    // t / 4 + 4 j, for j = 0..3: so lane i of the group addresses key base + i / 4,
+    // channels 32 cb + 16 ((l / 16) % 2) + 4 (i % 4) .. + 3.
     uint4 va[kD / 32][4];
+    const int tr_row = (lane % 16) / 4;
+    const int tr_col = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 #pragma unroll
     for (int cb = 0; cb < kD / 32; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint16_t* vrow = &vl[(32 * cb + col) * kVRow + 16 * ks + 4 * half];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        va[cb][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int key = 16 * ks + 8 * e + 4 * half + tr_row;
+          const int ch = 32 * cb + tr_col;
+          const uint16_t* a = &vl[key * kD + 8 * v_slot(key, ch / 8) + ch % 8];
+          const i16x4_t t = __builtin_bit_cast(
+              i16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) i16x4_t*)a));
+          w[2 * e] = uint32_t(uint16_t(t[0])) | (uint32_t(uint16_t(t[1])) << 16);
+          w[2 * e + 1] = uint32_t(uint16_t(t[2])) | (uint32_t(uint16_t(t[3])) << 16);
+        }
+        va[cb][ks] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     softmax_head(kt, 1, s1);
 #pragma unroll
@@ -395,27 +450,91 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
       for (int cb = 0; cb < kD / 32; ++cb) acc[1][cb] = mfma<DT>(va[cb][ks], pb1[ks], acc[1][cb]);
   };
 
-  // Step j: group g takes tile 2j + g from buffer j % 2 while every wave
-  // stages step j + 1 into the other buffer; one barrier per step.
-  stage_load(0);
-  stage_store(0);
-  stage_load(1);
-  __syncthreads();
-  for (int j = 0; j < n_steps; ++j) {
+  // Step j: group g takes tile 2j + g from buffer j % kStages; the loads of
+  // step j + 2 are issued before it (into the buffer step j - 1 used, free
+  // since the last barrier) and must land, with step j + 1's, before step
+  // j + 2; each step waits only for step j + 1's loads. One barrier per step.
+  //
+  // The three buffers of a step are distinct, and are passed as restrict
+  // pointers: the compiler then knows the direct loads of step j + 2 do not
+  // write what step j reads, and does not wait for them before every LDS read
+  // (it would otherwise, and the prefetch would be lost). The loop-carried
+  // order -- step j + 2's loads land before step j + 2 reads them -- is kept
+  // by the explicit counter waits and barriers, which are plain s_barrier
+  // (a fence would also wait for the loads in flight) after an LDS-counter
+  // wait for this wave's own LDS writes.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto step = [&](int j, const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
+                  uint16_t* __restrict__ dma_k, uint16_t* __restrict__ dma_v,
+                  const uint16_t* __restrict__ rd_k, const uint16_t* __restrict__ rd_v,
+                  uint16_t* __restrict__ fix_v, const int32_t* __restrict__ tb) {
+    if (j + 2 < n_steps) {
+      const int b = block_of(j + 2);
+      const int phys =
+          b < kTabCache ? bt_row.phys(__builtin_amdgcn_readfirstlane(tb[b]), b) : bt_row[b];
+      stage_issue(phys, gk, gv, dma_k, dma_v);
+    }
     const int kt = NG * j + grp;
-    if (kt < unit_tiles) tile_step(kt, k_lds[j % 2][grp], vt_lds[j % 2][grp]);
-    stage_store(j + 1);
-    stage_load(j + 2);
-    __syncthreads();
+    if (kt < unit_tiles) tile_step(kt, rd_k, rd_v);
+    if (j + 1 < n_steps) {
+      wait_loads(j + 2 < n_steps);
+      stage_fix(j + 1, fix_v);
+    }
+  };
+  const uint16_t* gk = static_cast<const uint16_t*>(p.k);
+  const uint16_t* gv = static_cast<const uint16_t*>(p.v);
+  // The table entries are copied to LDS in the prologue, their reads issued
+  // with the first two stages' loads (the copy then waits for both, once per
+  // workgroup); a step reads its entry from LDS instead of waiting for a
+  // scalar load of it from global memory.
+  const int n_tab = nb < kTabCache ? nb : kTabCache;
+  constexpr int kTabPerThread = kTabCache / (kPrefillWaves * kWaveSize);
+  static_assert(kTabPerThread * kPrefillWaves * kWaveSize == kTabCache, "table copy");
+  auto prologue = [&](const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
+                      uint16_t* __restrict__ k0, uint16_t* __restrict__ v0,
+                      uint16_t* __restrict__ k1, uint16_t* __restrict__ v1,
+                      int32_t* __restrict__ tb) {
+    stage_issue(bt_row[block_of(0)], gk, gv, k0, v0);
+    int32_t tab_v[kTabPerThread];
+#pragma unroll
+    for (int i = 0; i < kTabPerThread; ++i) {
+      const int b = int(threadIdx.x) + i * kPrefillWaves * kWaveSize;
+      tab_v[i] = bt_row.raw(b < n_tab ? b : n_tab - 1);   // no branch: the wait stays at the write
+    }
+    if (1 < n_steps) stage_issue(bt_row[block_of(1)], gk, gv, k1, v1);
+#pragma unroll
+    for (int i = 0; i < kTabPerThread; ++i) tb[int(threadIdx.x) + i * kPrefillWaves * kWaveSize] = tab_v[i];
+  };
+  prologue(gk, gv, k_lds[0][grp], v_lds[0][grp], k_lds[1][grp], v_lds[1][grp], tab);
+  wait_loads(1 < n_steps);
+  stage_fix(0, v_lds[0][grp]);
+  barrier();
+  // Unrolled by the buffer count, so each step's buffers are fixed offsets
+  // and the operand addresses need no per-step arithmetic.
+  static_assert(kStages == 3, "unrolled by three");
+  for (int j = 0; j < n_steps; j += 3) {
+    step(j, gk, gv, k_lds[2][grp], v_lds[2][grp], k_lds[0][grp], v_lds[0][grp], v_lds[1][grp], tab);
+    barrier();
+    if (j + 1 >= n_steps) break;
+    step(j + 1, gk, gv, k_lds[0][grp], v_lds[0][grp], k_lds[1][grp], v_lds[1][grp], v_lds[2][grp], tab);
+    barrier();
+    if (j + 2 >= n_steps) break;
+    step(j + 2, gk, gv, k_lds[1][grp], v_lds[1][grp], k_lds[2][grp], v_lds[2][grp], v_lds[0][grp], tab);
+    barrier();
   }
 
   // Merge the two groups' states of each unit through LDS (the staging
   // buffers are free now), one query block at a time: group 1 writes, group 0
   // combines and stores.
   float* xa = reinterpret_cast<float*>(&k_lds[0][0][0]);      // [NU][kD/32][16][64]
-  float* xm = reinterpret_cast<float*>(&vt_lds[0][0][0]);     // [NU][2][64]
+  float* xm = reinterpret_cast<float*>(&v_lds[0][0][0]);      // [NU][2][64]
   static_assert(NU * (kD / 32) * 16 * kWaveSize * 4 <= sizeof(k_lds), "merge space");
-  static_assert(NU * 2 * kWaveSize * 4 <= sizeof(vt_lds), "merge space");
+  static_assert(NU * 2 * kWaveSize * 4 <= sizeof(v_lds), "merge space");
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (grp == 1) {

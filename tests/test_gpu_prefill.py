@@ -100,3 +100,10 @@ def test_rows_beyond_the_plan_grid_give_nan():
     assert torch.isnan(out[256:300].float()).all()
     H.assert_close(out[:256], ref[:256], "bf16", "covered rows of sequence 0")
     H.assert_close(out[300:], ref[300:], "bf16", "sequence 1")
+
+
+def test_history_longer_than_the_table_copy():
+    """Histories of 20000 and 16500 keys (1250 and 1032 blocks of 16): a
+    workgroup copies the first 1024 table entries to LDS and reads the
+    blocks past them from the table in global memory."""
+    _run(wl.custom(74, [20000, 16500], n_q=[40, 70], hq=4, hkv=1, d=64, dtype="bf16"))
