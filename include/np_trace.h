@@ -66,6 +66,18 @@ extern "C" {
 #define NP_TRACE_SK_SLOTS 768
 #define NP_TRACE_SK_MERGE0 (8 + 8 * NP_TRACE_SK_PIECES)
 #define NP_TRACE_SK_MERGE_WORDS (8 + NP_TRACE_SK_SLOTS)
+/*
+ * Stream-K timestamps (s_memrealtime, 100 MHz; low word, then high word; 0 if
+ * not reached), from word NP_TRACE_SK_STAMP0 of the workgroup's record, taken
+ * by wave 0 after waiting for its outstanding memory operations:
+ *   [0] start  [2] schedule known (length scan done)  [4] pieces done
+ *   [6] end (merges done)
+ *   piece i < NP_TRACE_SK_PIECES: [8 + 4 i] start, [10 + 4 i] partial or
+ *     output written (and, for a shared segment, its ticket taken)
+ *   merge j < 2: [8 + 4 NP_TRACE_SK_PIECES + 4 j] start, [+ 2] end
+ */
+#define NP_TRACE_SK_STAMP0 (NP_TRACE_SK_MERGE0 + 2 * NP_TRACE_SK_MERGE_WORDS)
+#define NP_TRACE_SK_STAMP_WORDS (8 + 4 * NP_TRACE_SK_PIECES + 8)
 #define NP_TRACE_SK_WORDS 2048
 
 /*

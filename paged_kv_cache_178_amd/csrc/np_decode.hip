@@ -1047,6 +1047,10 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
   static_assert(NW % HW == 0, "heads per workgroup must divide the waves");
   __shared__ int sk_pre[kSkMaxSeqs + 1];    // units before each sequence's segments
   __shared__ int sk_last;
+#ifdef NP_TRACE
+  static_assert(NP_TRACE_SK_STAMP0 + NP_TRACE_SK_STAMP_WORDS <= NP_TRACE_SK_WORDS, "trace record");
+  const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
+#endif
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int w = blockIdx.x;
@@ -1099,8 +1103,24 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
     trec[5] = C;
     trec[6] = trec[7] = 0;
   };
+  // Timestamp at word `at` of the stamp area (wave 0 waits for its memory
+  // operations first; the other waves run on).
+  auto sk_stamp = [&](int at, uint64_t t = 0) {
+    if (trec == nullptr || threadIdx.x >= kWaveSize) return;
+    if (t == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      t = __builtin_amdgcn_s_memrealtime();
+    }
+    if (threadIdx.x == 0) {
+      trec[NP_TRACE_SK_STAMP0 + at] = int32_t(uint32_t(t));
+      trec[NP_TRACE_SK_STAMP0 + at + 1] = int32_t(uint32_t(t >> 32));
+    }
+  };
+  sk_stamp(0, t_entry);
+  sk_stamp(2);
   if (u >= u_end) {
     trace_header(0);
+    sk_stamp(6);
     return;
   }
 #else
@@ -1142,6 +1162,9 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
       u = seg_end < u_end ? seg_end : u_end;
       continue;
     }
+#ifdef NP_TRACE
+    if (t_pieces < NP_TRACE_SK_PIECES) sk_stamp(8 + 4 * t_pieces);
+#endif
     // Lane coordinates are derived afresh in every piece (from an opaque copy
     // of the thread index) so the compiler does not hoist lane-dependent
     // addresses out of the loop and keep them live across it.
@@ -1238,10 +1261,14 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
       }
     }
 #ifdef NP_TRACE
+    if (t_pieces < NP_TRACE_SK_PIECES) sk_stamp(10 + 4 * t_pieces);
     ++t_pieces;
 #endif
     u = seg_end < u_end ? seg_end : u_end;
   }
+#ifdef NP_TRACE
+  sk_stamp(4);
+#endif
   for (int i = 0; i < n_merge; ++i) {
     const int ms = i ? mg_s[1] : mg_s[0];
     const int mh = i ? mg_hg[1] : mg_hg[0];
@@ -1268,9 +1295,15 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
       if (mn > NP_TRACE_SK_SLOTS) t_overflow = 1;
     }
 #endif
+#ifdef NP_TRACE
+    sk_stamp(8 + 4 * NP_TRACE_SK_PIECES + 4 * i);
+#endif
     merge_pieces<DT, D_PAD, HW * G>(p, ms, mh * HW * G, mn, [&](int j, int h) {
       return int64_t(slot_of(j)) * (HW * G) + h;
     });
+#ifdef NP_TRACE
+    sk_stamp(10 + 4 * NP_TRACE_SK_PIECES + 4 * i);
+#endif
     // The next call that uses the counter is ordered after this launch.
     if (threadIdx.x == 0)
       __hip_atomic_store(p.ws_cnt + int64_t(ms * p.hkv + mh) * kCounterStride, 0u,
@@ -1278,6 +1311,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
   }
 #ifdef NP_TRACE
   trace_header(n_merge);
+  sk_stamp(6);
 #endif
 }
 

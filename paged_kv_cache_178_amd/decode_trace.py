@@ -1,4 +1,4 @@
-"""Phase timeline of the uniform-split decode, from the trace build.
+"""Phase timelines of the decode kernels, from the trace build.
 
 Runs the batch-1 decode of the Llama-3.2-1B head shape (Hq 32, Hkv 8, d 64,
 bf16, block size 16) through libnp_paged_trace.so, which stamps every
@@ -9,6 +9,14 @@ and the same for the workgroup that merged the splits of each KV head (the
 critical path). Every launch reads its own cold copy of the pool.
 
     python -m paged_kv_cache_178_amd.decode_trace --history 4096 --reps 40
+
+With --batching it runs the continuous-batching workload (64 ragged
+sequences) through the stream-K kernel instead and prints, per launch
+(median over launches), when workgroups start and know their schedule, how
+long their pieces and merges take, and when they end: the spread of the end
+times against the time spent reading is the schedule's loss.
+
+    python -m paged_kv_cache_178_amd.decode_trace --batching --reps 10
 
 The trace build waits for all outstanding memory operations at every stamp,
 so its total is an upper bound of the product kernel's; the phase split is
@@ -138,12 +146,136 @@ def report(res) -> str:
     return "\n".join(lines)
 
 
+SK_WORDS = 2048                          # NP_TRACE_SK_WORDS
+SK_PIECES = 32                           # NP_TRACE_SK_PIECES
+SK_STAMP0 = 8 + 8 * 32 + 2 * (8 + 768)   # NP_TRACE_SK_STAMP0
+SK_STAMP_WORDS = 8 + 4 * 32 + 8
+
+
+def parse_sk(buf):
+    """Stream-K records of one launch (numpy int32 [wgs, SK_WORDS]): per
+    workgroup its piece and merge counts and its stamps in 10 ns ticks
+    (0 where not reached)."""
+    import numpy as np
+
+    recs = []
+    for w in buf:
+        st = w[SK_STAMP0:SK_STAMP0 + SK_STAMP_WORDS]
+        t = (st[1::2].astype(np.uint32).astype(np.uint64) << np.uint64(32)) | \
+            st[0::2].astype(np.uint32).astype(np.uint64)
+        n_p = min(int(w[0]), SK_PIECES)
+        n_m = int(w[1])
+        recs.append(dict(where=int(w[2]), pieces=n_p, merges=n_m,
+                         start=int(t[0]), sched=int(t[1]), loop_end=int(t[2]), end=int(t[3]),
+                         piece=[(int(t[4 + 2 * i]), int(t[5 + 2 * i])) for i in range(n_p)],
+                         merge=[(int(t[4 + 2 * SK_PIECES + 2 * j]),
+                                 int(t[5 + 2 * SK_PIECES + 2 * j])) for j in range(n_m)]))
+    return recs
+
+
+def summarize_sk(launches):
+    """Medians over launches of the per-launch figures (µs)."""
+    import numpy as np
+
+    keys = ["span (first start to last end)", "start spread (last start)",
+            "schedule known (median, from own start)", "first piece start (median, from own start)",
+            "pieces per workgroup (mean)", "piece time (median)", "piece time (max)",
+            "gap between pieces (median)", "reading done (median end of pieces)",
+            "reading done (latest)", "merges per launch", "merge time (median)",
+            "merge time (max)", "end (median)", "end (90th percentile)", "end (latest)",
+            "busy fraction (pieces / (end - start), median)"]
+    vals = {k: [] for k in keys}
+    for recs in launches:
+        t0 = min(r["start"] for r in recs)
+        us = lambda t: (t - t0) / 100.0
+        ends = [us(r["end"]) for r in recs]
+        pieces = [(b - a) / 100.0 for r in recs for a, b in r["piece"] if a and b]
+        gaps = [(r["piece"][i + 1][0] - r["piece"][i][1]) / 100.0 for r in recs
+                for i in range(len(r["piece"]) - 1) if r["piece"][i][1] and r["piece"][i + 1][0]]
+        merges = [(b - a) / 100.0 for r in recs for a, b in r["merge"] if a and b]
+        busy = [sum(b - a for a, b in r["piece"]) / max(1, r["end"] - r["start"])
+                for r in recs if r["piece"]]
+        firsts = [(r["piece"][0][0] - r["start"]) / 100.0 for r in recs if r["piece"]]
+        done = [us(r["loop_end"]) for r in recs if r["loop_end"]]
+        row = [max(ends), max(us(r["start"]) for r in recs),
+               float(np.median([(r["sched"] - r["start"]) / 100.0 for r in recs])),
+               float(np.median(firsts)) if firsts else math.nan,
+               float(np.mean([r["pieces"] for r in recs])),
+               float(np.median(pieces)) if pieces else math.nan,
+               max(pieces) if pieces else math.nan,
+               float(np.median(gaps)) if gaps else math.nan,
+               float(np.median(done)) if done else math.nan, max(done) if done else math.nan,
+               len(merges), float(np.median(merges)) if merges else math.nan,
+               max(merges) if merges else math.nan, float(np.median(ends)),
+               float(np.percentile(ends, 90)), max(ends),
+               float(np.median(busy)) if busy else math.nan]
+        for k, v in zip(keys, row):
+            vals[k].append(v)
+    return [(k, float(np.median(v))) for k, v in vals.items()]
+
+
+def run_batching(reps: int, copies: int = 2):
+    import torch
+
+    from paged_kv_cache_178_amd import binding
+    from paged_kv_cache_178_amd import workloads as wl
+
+    lib = binding.trace_library()
+    dev = torch.device("cuda:0")
+    inp = wl.continuous_batching()
+    q = inp.q.to(dev)
+    bt = inp.block_table.to(dev)
+    lens = inp.context_lens.to(dev)
+    ks = [inp.k_pool.to(dev) for _ in range(copies)]
+    vs = [inp.v_pool.to(dev) for _ in range(copies)]
+    out = torch.empty_like(q)
+    desc = binding.make_desc(q, ks[0], bt, out=out, scale=inp.scale)
+    plan = binding.np_plan(desc, inp.context_lens.numpy(), None, lib=lib)
+    if plan.schedule != 2:
+        raise SystemExit("the default plan of the batching workload is not stream-K")
+    ws = binding.workspace_for(plan, dev)
+    grid, wg, comb = plan.launch_shape()
+    n_wg = grid[0] * grid[1] * grid[2]
+    trace = torch.zeros(n_wg * SK_WORDS, dtype=torch.int32, device=dev)
+    st = lib.np_debug_set_trace(trace.data_ptr(), trace.numel() * 4)
+    if st:
+        raise binding.NPError(st, "np_debug_set_trace")
+    launches = []
+    try:
+        for r in range(reps + 2):
+            trace.zero_()
+            c = r % copies
+            binding.np_paged_attention_decode(desc, plan, q, ks[c], vs[c], bt, lens, out, ws)
+            torch.cuda.synchronize()
+            if r >= 2:
+                launches.append(parse_sk(trace.view(n_wg, SK_WORDS).cpu().numpy()))
+    finally:
+        lib.np_debug_set_trace(None, 0)
+    return dict(grid=grid, units=plan.blocks_per_split, copies=copies, launches=launches,
+                rows=summarize_sk(launches), kv_bytes=inp.kv_bytes())
+
+
+def report_sk(res) -> str:
+    lines = [f"stream-K decode trace: continuous batching (64 sequences, "
+             f"{res['kv_bytes'] / 1e6:.0f} MB of K/V), grid {list(res['grid'])}, "
+             f"{res['units']} units per workgroup, {len(res['launches'])} launches on "
+             f"{res['copies']} alternating pool copies", "", "| figure | µs (or count) |", "|---|---|"]
+    for k, v in res["rows"]:
+        lines.append(f"| {k} | {v:.2f} |")
+    return "\n".join(lines)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--history", type=int, default=4096)
     ap.add_argument("--reps", type=int, default=40)
     ap.add_argument("--blocks-per-split", type=int, default=0)
+    ap.add_argument("--batching", action="store_true",
+                    help="stream-K timeline of the continuous-batching workload")
     args = ap.parse_args(argv)
+    if args.batching:
+        print(report_sk(run_batching(args.reps)), flush=True)
+        return 0
     res = run(args.history, args.reps, bps=args.blocks_per_split)
     print(report(res), flush=True)
     return 0
