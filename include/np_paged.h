@@ -112,8 +112,7 @@ typedef struct np_paged_desc {
 /* Planner knobs; pass NULL for the defaults. */
 typedef struct np_plan_opts {
   int32_t num_cus;                /* compute units to fill; 0 => 256           */
-  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 1 (uniform
-                                     splits) or 2 (stream-K)                   */
+  int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 1          */
   int32_t min_blocks_per_split;   /* 0 => 4 (uniform); stream-K: least units
                                      per workgroup, 0 => 8                     */
   int32_t max_blocks_per_split;   /* 0 => 1024 tokens' worth of blocks         */
@@ -272,7 +271,7 @@ np_status np_paged_attention_decode(const np_paged_desc* desc, const np_plan_t* 
  * library-owned 8 MiB device array, one per GPU, held until the process
  * ends. A plan whose np_plan_workspace_bytes exceeds 8 MiB returns
  * NP_ERR_WORKSPACE_TOO_SMALL before anything is launched (the 64-sequence
- * stream-K plan of the Llama head shape needs 4.3 MB). The first call on a
+ * stream-K plan of the Llama head shape needs 2.3 MB). The first call on a
  * device looks the array up and clears it with a fill kernel on `stream`;
  * make that first call outside graph capture to keep the clear out of a
  * captured graph. Every call on a GPU shares that GPU's array, so calls that

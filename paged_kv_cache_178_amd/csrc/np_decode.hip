@@ -505,7 +505,7 @@ __device__ __forceinline__ void pv_pair(const uint4& va, const uint4& vb, const 
 // ------------------------------------------------------------------ kernel
 
 // Tile constants of one instantiation.
-template <int DT, int D_PAD, int BS>
+template <int DT, int D_PAD, int BS, int NWAVES = kDecodeWaves>
 struct DecodeShape {
   static constexpr int kElt = Elt<DT>::kBytes;
   static constexpr int VEC = 16 / kElt;          // elements per lane-load
@@ -515,7 +515,7 @@ struct DecodeShape {
   static constexpr int NLB = BS / TPL;           // wave-loads per block (per K or V)
   static_assert(NLB % 2 == 0, "slots of a block are paired for P.V");
   static constexpr int NG = 4 / NLB > 1 ? 4 / NLB : 1;   // blocks per load group
-  static constexpr int NW = kDecodeWaves;
+  static constexpr int NW = NWAVES;             // waves per workgroup
 };
 
 // Online-softmax state of one lane: m[h] is shared by the whole wave
@@ -677,12 +677,12 @@ __device__ __forceinline__ void wave_accumulate(
 // head h of the workgroup's HW * G (c < head_dim), emit(h, c, t0, t1, M, l)
 // with the unnormalised sums. One barrier, plus one before the LDS writes
 // when the workgroup reuses the buffers (sync_before).
-template <int DT, int D_PAD, int G, int BS, int HW, typename Emit>
+template <int DT, int D_PAD, int G, int BS, int HW, int NWAVES = kDecodeWaves, typename Emit>
 __device__ __forceinline__ void wg_combine(const DecodeParams& p, const int wave, const int lane,
                                            const int row, const int ch0,
                                            const LaneState<G, DecodeShape<DT, D_PAD, BS>::VEC>& st,
                                            const bool sync_before, Emit&& emit) {
-  using S = DecodeShape<DT, D_PAD, BS>;
+  using S = DecodeShape<DT, D_PAD, BS, NWAVES>;
   constexpr int VEC = S::VEC, LPR = S::LPR, TPL = S::TPL, NW = S::NW;
   const float(&m)[G] = st.m;
   const float(&l)[G] = st.l;
@@ -989,12 +989,12 @@ constexpr int sk_min_waves(int dt, int d_pad, int g) {
 // thread owns float4 chunks of the GG x d_pad output and folds in all pieces
 // (UB loads in flight at a time), with the split-KV page's log-sum-exp
 // weights as in merge_splits. No LDS, no barrier.
-template <int DT, int D_PAD, int GG, typename PartOf>
+template <int DT, int D_PAD, int GG, int NWAVES, typename PartOf>
 __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int head0, int n,
                                              PartOf&& part_of) {
   constexpr int NCH = GG * D_PAD / 4;
   constexpr int UB = 4;
-  for (int chunk = threadIdx.x; chunk < NCH; chunk += kDecodeWaves * kWaveSize) {
+  for (int chunk = threadIdx.x; chunk < NCH; chunk += NWAVES * kWaveSize) {
     const int h = (chunk * 4) / D_PAD;
     const int c = (chunk * 4) % D_PAD;
     float mx = -INFINITY, d = 0.0f;
@@ -1038,10 +1038,10 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int h
 }
 
 template <int DT, int D_PAD, int G, int BS, int HW>
-__global__ __launch_bounds__(kDecodeWaves * kWaveSize)
+__global__ __launch_bounds__(kSkWaves * kWaveSize)
 __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_decode_sk_kernel(
     const DecodeParams p) {
-  using S = DecodeShape<DT, D_PAD, BS>;
+  using S = DecodeShape<DT, D_PAD, BS, kSkWaves>;
   constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, NG = S::NG, NW = S::NW;
   constexpr int WPH = NW / HW;              // waves per head
   static_assert(NW % HW == 0, "heads per workgroup must divide the waves");
@@ -1208,7 +1208,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
     const bool direct = n_pieces == 1;
     const int slot = 2 * w + (u == w * C ? 0 : 1);
     const int head0 = hg * HW * G;            // first query head of the segment
-    wg_combine<DT, D_PAD, G, BS, HW>(
+    wg_combine<DT, D_PAD, G, BS, HW, kSkWaves>(
         p, wave, lane, row, ch0, st, !first_piece,
         [&](int h, int c, float t0, float t1, float mm, float ll) {
           if (direct) {
@@ -1298,7 +1298,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
 #ifdef NP_TRACE
     sk_stamp(8 + 4 * NP_TRACE_SK_PIECES + 4 * i);
 #endif
-    merge_pieces<DT, D_PAD, HW * G>(p, ms, mh * HW * G, mn, [&](int j, int h) {
+    merge_pieces<DT, D_PAD, HW * G, kSkWaves>(p, ms, mh * HW * G, mn, [&](int j, int h) {
       return int64_t(slot_of(j)) * (HW * G) + h;
     });
 #ifdef NP_TRACE

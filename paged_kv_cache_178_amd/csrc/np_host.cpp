@@ -210,7 +210,7 @@ void plan_stream_k(np_plan_core& c, const int32_t* lens, const np_plan_opts& o) 
   c.max_rows = 1;
   c.grid[0] = static_cast<uint32_t>(W);
   c.grid[1] = c.grid[2] = 1;
-  c.wg_size = kDecodeWaves * kWaveSize;
+  c.wg_size = kSkWaves * kWaveSize;
   c.fused_combine = 1;
   c.combine_wgs = 0;
   // Counters, then two partial slots per workgroup, each of HW * G query

@@ -25,7 +25,8 @@ constexpr int kScheduleUniform = 1;            // decode: uniform page-aligned s
 constexpr int kScheduleStreamK = 2;            // decode: equal work per workgroup
 constexpr int kSkMaxSeqs = 2048;               // stream-K: sequences per launch
 constexpr int kSkDefaultCost = 4;              // stream-K: virtual blocks per segment
-constexpr int kSkWgsPerCu = 2;                 // stream-K: resident decode workgroups per CU
+constexpr int kSkWaves = 8;                    // waves per stream-K decode workgroup
+constexpr int kSkWgsPerCu = 1;                 // stream-K: resident decode workgroups per CU
 constexpr int kSkMinUnits = 8;                 // stream-K: least units per workgroup
 constexpr int kTraceStamps = NP_TRACE_STAMPS;  // trace build: phase stamps per workgroup
 

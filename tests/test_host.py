@@ -223,7 +223,7 @@ def test_decode_plan_matches_model(seed):
         assert plan.workspace_bytes == 0
 
 
-def model_stream_k_plan(lens, bs, hkv, max_blocks, cost=4, num_cus=256, per_cu=2,
+def model_stream_k_plan(lens, bs, hkv, max_blocks, cost=4, num_cus=256, per_cu=1,
                         min_units=8):
     """Brute force: a workgroup serves hw KV heads (the largest of 4, 2, 1
     dividing Hkv); segments are (sequence, head group); intersect every
@@ -273,7 +273,7 @@ def test_stream_k_plan_matches_model(seed):
     plan = B.np_plan(d, lens, None, opts)
     W, C, items, hw = model_stream_k_plan(lens.tolist(), bs, hkv, max_blocks, **kw)
     assert plan.schedule == 2
-    assert plan.launch_shape() == ((W, 1, 1), 256, 0)
+    assert plan.launch_shape() == ((W, 1, 1), 512, 0)
     assert plan.blocks_per_split == C
     assert plan.work_items() == items
     # Every (sequence, KV head, block) exactly once; no workgroup over C units.
