@@ -19,7 +19,28 @@ from tests import sk_model
 pytestmark = pytest.mark.gpu
 
 SK_WORDS, SK_PIECES, SK_MERGE0, SK_MERGE_WORDS = 2048, 32, 8 + 8 * 32, 8 + 768
+SK_STAMP0 = SK_MERGE0 + 2 * SK_MERGE_WORDS
 UNI_WORDS = 32
+
+
+def sk_stamps_in_order(r):
+    """The stream-K record's timestamps (np_trace.h: start, schedule known,
+    each piece's start and publish, pieces done, each merge, end) are all
+    taken and never go back in time (s_memrealtime is one clock for the
+    whole device)."""
+    def t(at):
+        lo, hi = int(r[SK_STAMP0 + at]) & 0xFFFFFFFF, int(r[SK_STAMP0 + at + 1]) & 0xFFFFFFFF
+        return (hi << 32) | lo
+    seq = [t(0), t(2)]
+    if t(4) == 0:   # a workgroup whose unit range is empty stops after the schedule
+        return int(r[0]) == 0 and int(r[1]) == 0 and 0 < t(0) <= t(2) <= t(6)
+    for i in range(min(int(r[0]), SK_PIECES)):
+        seq += [t(8 + 4 * i), t(10 + 4 * i)]
+    seq.append(t(4))
+    for j in range(int(r[1])):
+        seq += [t(8 + 4 * SK_PIECES + 4 * j), t(10 + 4 * SK_PIECES + 4 * j)]
+    seq.append(t(6))
+    return all(x > 0 for x in seq) and all(a <= b for a, b in zip(seq, seq[1:]))
 
 
 def run_traced(inp, opts, words):
@@ -77,6 +98,8 @@ def test_stream_k_trace_matches_plan(case):
         r = rec[w]
         assert r[3] == 0, f"workgroup {w}: trace overflow"
         assert (r[4], r[5]) == (U, C), w
+        assert sk_stamps_in_order(r), f"workgroup {w}: timestamps"
+
         n = int(r[0])
         got = [tuple(int(x) for x in r[8 + 8 * i: 8 + 8 * i + 7]) for i in range(n)]
         # (sequence, head group, first, end, slot, pieces, ticket, first unit)
