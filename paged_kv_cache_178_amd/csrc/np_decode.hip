@@ -977,10 +977,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 // the schedule always matches the lengths the kernel reads and the workspace
 // bounds depend only on W.
 
-// Waves per SIMD the stream-K kernel is compiled for: three resident
-// workgroups per CU where the registers allow it without spilling (head_dim 64
-// with up to 4 heads per group, 16-bit head_dim 128 with up to 3), else no
-// constraint. The planner's default of two workgroups per CU holds for all.
+// Waves per SIMD the stream-K kernel is compiled for: three where the
+// registers allow it without spilling (head_dim 64 with up to 4 heads per
+// group, 16-bit head_dim 128 with up to 3), else no constraint. The planner's
+// default, one 8-wave workgroup per CU, needs two; the tighter register limit
+// measured no slower.
 constexpr int sk_min_waves(int dt, int d_pad, int g) {
   return (d_pad == 64 && g <= 4) || (d_pad == 128 && dt != NP_F32 && g <= 3) ? 3 : 1;
 }
