@@ -56,6 +56,8 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_llama_L4096_pmc.md")
 PMC_SUMMARY_BATCHING = os.path.join(ROOT, "profiles", "paged_decode_batching_64seq_pmc.md")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_decode.hip")
 HOST_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_host.cpp")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_178_amd", "csrc", "np_prefill.hip")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "paged_prefill_chunked_4x2560_counters.md")
 
 
 def log(msg: str) -> None:
@@ -70,6 +72,30 @@ def kernel_source_sha() -> str:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def prefill_source_sha() -> str:
+    """Digest of the prefill kernel's source and of the planner."""
+    h = hashlib.sha256()
+    for path in (PREFILL_SRC, HOST_SRC):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_mfma_busy(path=PREFILL_COUNTERS):
+    """Fraction of SIMD cycles the matrix cores were busy during the chunked
+    prefill, from the committed counter summary, if it was taken on the
+    current prefill source; else None."""
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^counters-json: (\{.*\})\s*$", open(path).read(), re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_sha") != prefill_source_sha():
+        return None
+    return rec.get("mfma_busy_frac")
 
 
 def stored_traffic(path=PMC_SUMMARY):
@@ -653,6 +679,10 @@ def run_prefill(args, dev, props) -> int:
         "parity_max_abs_err": float(err.max()),
         "device": props.name,
     }
+    busy = stored_mfma_busy()
+    rec["mfma_busy"] = None if busy is None else {
+        "frac": busy, "counters": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC x SIMDs)",
+        "from": os.path.relpath(PREFILL_COUNTERS, ROOT)}
     if not args.no_cpu_baseline:
         best, sample, threads = cpu_baseline(inp, args.cpu_seconds, seqs=[0], prefill=True)
         sub = wl.PagedInputs(**{**inp.__dict__, "context_lens": inp.context_lens[:1],

@@ -1,7 +1,9 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
 stats:    kernel-trace statistics (calls, average/min/max duration per kernel).
-counters: median per-dispatch value of every counter collected for one kernel.
+counters: median per-dispatch value of every counter collected for one kernel
+       (with --simds and --xccs, also the fraction of SIMD cycles the matrix
+       cores were busy; with --sha, stamped for the benchmark to read).
 pmc:      HBM traffic per launch of one kernel from two counter runs
        (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by what the
        same counter reads for a plain copy of known size in the same run.
@@ -9,7 +11,7 @@ pmc:      HBM traffic per launch of one kernel from two counter runs
 Usage:
   python -m paged_kv_cache_178_amd.rocprof_summary stats STATS_CSV --out FILE --cmd "..."
   python -m paged_kv_cache_178_amd.rocprof_summary counters CSV [CSV ...] --kernel SUBSTR \
-      --out FILE --cmd "..."
+      --out FILE --cmd "..." [--simds N --xccs N --sha SHA]
   python -m paged_kv_cache_178_amd.rocprof_summary pmc --fetch CSV --write CSV \
       --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes N --kv-bytes N --sha SHA \
       --out FILE --cmd "..."
@@ -54,7 +56,29 @@ def counters(args) -> None:
              "|---|---|---|"]
     for name in sorted(vals):
         lines.append(f"| `{name}` | {len(vals[name])} | {statistics.median(vals[name]):.0f} |")
+    busy = mfma_busy_frac(vals, args.simds, args.xccs)
+    if busy is not None:
+        lines += ["", f"- MFMA busy: {100 * busy:.1f}% of the SIMD cycles while the GPU was active "
+                      f"(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xccs} XCCs x "
+                      f"{args.simds} SIMDs), medians per dispatch)"]
+        if args.sha:
+            lines.append("counters-json: " + json.dumps({"kernel_sha": args.sha,
+                                                         "mfma_busy_frac": round(busy, 4)}))
     open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def mfma_busy_frac(vals, simds, xccs):
+    """Fraction of SIMD cycles the matrix cores were busy: the busy cycles
+    summed over all SIMDs, over the GPU-active cycles of one XCC (the
+    per-dispatch value sums the XCCs) times the SIMD count. None without the
+    two counters or the device sizes."""
+    if not simds or not xccs:
+        return None
+    if "SQ_VALU_MFMA_BUSY_CYCLES" not in vals or "GRBM_GUI_ACTIVE" not in vals:
+        return None
+    busy = statistics.median(vals["SQ_VALU_MFMA_BUSY_CYCLES"])
+    active = statistics.median(vals["GRBM_GUI_ACTIVE"]) / xccs
+    return busy / (active * simds) if active > 0 else None
 
 
 def _per_dispatch(path, counter, substr):
@@ -124,6 +148,9 @@ def main(argv=None) -> None:
     c.add_argument("--out", required=True)
     c.add_argument("--cmd", required=True)
     c.add_argument("--title", default="")
+    c.add_argument("--sha", default="")
+    c.add_argument("--simds", type=int, default=0)
+    c.add_argument("--xccs", type=int, default=0)
     b = sub.add_parser("pmc")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
