@@ -155,30 +155,10 @@ __device__ __forceinline__ float dot16<NP_F32>(const uint4& a, const uint4& b, f
   return c;
 }
 
-// Unpack a 16-byte chunk into fp32 values (8 for 16-bit types, 4 for fp32).
+// Unpack a 16-byte chunk into fp32 values (the fp32 path; 16-bit types use
+// packed v_dot2 on the raw words instead).
 template <int DT>
 __device__ __forceinline__ void unpack16(const uint4& a, float* f);
-
-template <>
-__device__ __forceinline__ void unpack16<NP_BF16>(const uint4& a, float* f) {
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-template <>
-__device__ __forceinline__ void unpack16<NP_F16>(const uint4& a, float* f) {
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
-    f[2 * i] = static_cast<float>(h.x);
-    f[2 * i + 1] = static_cast<float>(h.y);
-  }
-}
 
 template <>
 __device__ __forceinline__ void unpack16<NP_F32>(const uint4& a, float* f) {
