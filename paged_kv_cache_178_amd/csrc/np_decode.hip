@@ -305,10 +305,11 @@ __device__ __forceinline__ uint4 load16_stream(const void* base, int64_t elem_of
 }
 
 // Split partials are published with agent-scope relaxed atomic stores and
-// read back with agent-scope relaxed atomic loads. On gfx950 these are plain
-// 64-bit global stores/loads with the device-coherence bit set, so the partials
-// bypass the per-XCD L2 and no L2 write-back or invalidate (what an agent-scope
-// fence costs, per workgroup) is needed. The writer waits for its stores to
+// read back with buffer loads that carry the device-scope cache bit (the bit
+// an agent-scope atomic load carries). On gfx950 both are plain stores and
+// loads with the device-coherence bit set, so the partials bypass the per-XCD
+// L2 and no L2 write-back or invalidate (what an agent-scope fence costs, per
+// workgroup) is needed. The writer waits for its stores to
 // complete before it takes its arrival ticket; the reader issues its loads only
 // after seeing that every other ticket was taken.
 __device__ __forceinline__ void publish2(float* p, float a, float b) {
@@ -317,11 +318,17 @@ __device__ __forceinline__ void publish2(float* p, float a, float b) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float2 fetch2(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
-}
+// Word 3 of a buffer descriptor for untyped loads: data format 32 bits
+// (a zero format makes untyped buffer loads return 0), no swizzle, no index
+// stride.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of a load that reads what other workgroups published with
+// agent-scope stores: the device-scope bit (sc1), the same bit an agent-scope
+// atomic load carries.
+constexpr int kDeviceScopeLoad = 16;
+
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 
 // Merge the splits of one (sequence, KV head): with M = max_j m_j,
 // out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j. This is the split-KV
@@ -331,15 +338,38 @@ __device__ __forceinline__ float2 fetch2(const float* p) {
 // Latency-parallel: waves take splits round-robin, each lane owns float4
 // chunks of the G x d_pad output, and a batch of UB splits has all its loads
 // in flight before any is used; the per-wave states are merged through LDS.
-template <int DT, int D_PAD, int G, typename PartOf>
+// The partials of query head kvh * G + h and split j sit at part
+// row0 + h * max_splits + j. Each lane's offset inside the head group's rows
+// is computed once; a split moves every lane by the same amount, which is a
+// scalar offset of a buffer load (one descriptor per head group), so issuing
+// a split's loads costs no vector address arithmetic. Every read stays in
+// the head group's rows: j < splits <= max_splits.
+template <int DT, int D_PAD, int G>
 __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int kvh, int splits,
-                                             PartOf&& part_of, bool write = true) {
+                                             bool write = true) {
   constexpr int NW = kDecodeWaves;
   constexpr int NCH = G * D_PAD / 4;          // float4 chunks of the output
   constexpr int CPL = (NCH + kWaveSize - 1) / kWaveSize;
   constexpr int UB = CPL > 1 ? 4 : 8;
-  const int wave = threadIdx.x / kWaveSize;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int lane = threadIdx.x % kWaveSize;
+  splits = __builtin_amdgcn_readfirstlane(splits);
+
+  const int64_t row0 = (int64_t(s) * p.hq + int64_t(kvh) * G) * p.max_splits;
+  const __amdgpu_buffer_rsrc_t r_acc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<void*>(p.ws_acc + row0 * D_PAD), 0, G * p.max_splits * D_PAD * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t r_ml = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<void*>(p.ws_ml + 2 * row0), 0, G * p.max_splits * 8, kBufferWord3);
+  int acc_off[CPL], ml_off[CPL];
+#pragma unroll
+  for (int ci = 0; ci < CPL; ++ci) {
+    // Lanes past the output re-read its last chunk and get weight 0.
+    const int chunk = lane + ci * kWaveSize;
+    const int cc = chunk < NCH ? chunk : NCH - 1;
+    const int h = (cc * 4) / D_PAD;
+    acc_off[ci] = (h * p.max_splits * D_PAD + (cc * 4) % D_PAD) * 4;
+    ml_off[ci] = h * p.max_splits * 8;
+  }
 
   float mw[CPL], dw[CPL];
   float4 nw[CPL];
@@ -351,42 +381,56 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
   }
   for (int j0 = wave; j0 < splits; j0 += NW * UB) {
     float2 ml[UB][CPL];
-    float2 a0[UB][CPL], a1[UB][CPL];
+    float4 a[UB][CPL];
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
-      const int j = j0 + u * NW;
+      // A split past the last re-reads the last one and gets weight 0, so
+      // the batch is issued without branches.
+      const int j = j0 + u * NW < splits ? j0 + u * NW : splits - 1;
 #pragma unroll
       for (int ci = 0; ci < CPL; ++ci) {
-        const int chunk = lane + ci * kWaveSize;
-        // Every lane loads (a split past the last re-reads the last one and
-        // gets weight 0), so the batch is issued without branches.
-        const int cc = chunk < NCH ? chunk : NCH - 1;
-        const int h = (cc * 4) / D_PAD;
-        const int c = (cc * 4) % D_PAD;
-        const int64_t part = part_of(j < splits ? j : splits - 1, h);
-        ml[u][ci] = fetch2(p.ws_ml + 2 * part);
-        a0[u][ci] = fetch2(p.ws_acc + part * D_PAD + c);
-        a1[u][ci] = fetch2(p.ws_acc + part * D_PAD + c + 2);
-        if (j >= splits || chunk >= NCH) ml[u][ci].x = -INFINITY;
+        const u32x2_t m2 = __builtin_amdgcn_raw_buffer_load_b64(r_ml, ml_off[ci], j * 8,
+                                                                 kDeviceScopeLoad);
+        const u32x4_t a4 = __builtin_amdgcn_raw_buffer_load_b128(r_acc, acc_off[ci],
+                                                                  j * D_PAD * 4, kDeviceScopeLoad);
+        ml[u][ci] = make_float2(__uint_as_float(m2.x), __uint_as_float(m2.y));
+        a[u][ci] = make_float4(__uint_as_float(a4.x), __uint_as_float(a4.y),
+                               __uint_as_float(a4.z), __uint_as_float(a4.w));
       }
     }
+    // Keep the whole batch of loads ahead of the first use: left to itself
+    // the scheduler may sink the last split's loads below the maximum, which
+    // costs one more memory round trip.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+#pragma unroll
+      for (int ci = 0; ci < CPL; ++ci)
+        if (j0 + u * NW >= splits || lane + ci * kWaveSize >= NCH) ml[u][ci].x = -INFINITY;
 #pragma unroll
     for (int ci = 0; ci < CPL; ++ci) {
       float mx = mw[ci];
 #pragma unroll
       for (int u = 0; u < UB; ++u) mx = fmaxf(mx, ml[u][ci].x);
-      if (mx == -INFINITY) continue;
-      const float a = __builtin_amdgcn_exp2f(mw[ci] - mx);
-      float d = dw[ci] * a;
-      float4 n = make_float4(nw[ci].x * a, nw[ci].y * a, nw[ci].z * a, nw[ci].w * a);
+      // A batch with no split in it (mx still -inf) must leave the state as
+      // it is: its weights are then exp2(-inf) = 0. This is a select, not a
+      // skip, so every load of the batch is consumed on every path. A load
+      // left pending at the loop's back edge (as a skip leaves it) makes the
+      // compiler guard its register at the top of the loop with a counter
+      // wait placed among the batch's loads, which holds the last loads back
+      // until the first ones have returned: a second memory round trip.
+      const float ms = mx == -INFINITY ? 0.0f : mx;
+      const float aw = __builtin_amdgcn_exp2f(mw[ci] - ms);
+      float d = dw[ci] * aw;
+      float4 n = make_float4(nw[ci].x * aw, nw[ci].y * aw, nw[ci].z * aw, nw[ci].w * aw);
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        const float w = __builtin_amdgcn_exp2f(ml[u][ci].x - mx);
+        const float w = __builtin_amdgcn_exp2f(ml[u][ci].x - ms);
         d = fmaf(w, ml[u][ci].y, d);
-        n.x = fmaf(w, a0[u][ci].x, n.x);
-        n.y = fmaf(w, a0[u][ci].y, n.y);
-        n.z = fmaf(w, a1[u][ci].x, n.z);
-        n.w = fmaf(w, a1[u][ci].y, n.w);
+        n.x = fmaf(w, a[u][ci].x, n.x);
+        n.y = fmaf(w, a[u][ci].y, n.y);
+        n.z = fmaf(w, a[u][ci].z, n.z);
+        n.w = fmaf(w, a[u][ci].w, n.w);
       }
       mw[ci] = mx;
       dw[ci] = d;
@@ -909,9 +953,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
     // the XCC's L2 instead of memory (measured: 0.2 us of the 4096-token
     // step).
     const bool is_last = last;
-    merge_splits<DT, D_PAD, G>(p, s, kvh, is_last ? splits : 1, [&](int j, int h) {
-      return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
-    }, is_last);
+    merge_splits<DT, D_PAD, G>(p, s, kvh, is_last ? splits : 1, is_last);
 #ifdef NP_TRACE
     if (!is_last) {
       trace_write();
@@ -970,44 +1012,63 @@ constexpr int sk_min_waves(int dt, int d_pad, int g) {
 // thread owns float4 chunks of the GG x d_pad output and folds in all pieces
 // (UB loads in flight at a time), with the split-KV page's log-sum-exp
 // weights as in merge_splits. No LDS, no barrier.
-template <int DT, int D_PAD, int GG, int NWAVES, typename PartOf>
+template <int DT, int D_PAD, int GG, int NWAVES, typename SlotOf>
 __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int head0, int n,
-                                             PartOf&& part_of) {
+                                             SlotOf&& slot_of) {
   constexpr int NCH = GG * D_PAD / 4;
   constexpr int UB = 4;
+  n = __builtin_amdgcn_readfirstlane(n);
+  // Piece j of head h is part slot_of(j) * GG + h. As in merge_splits, the
+  // slot (the same for every lane) is a scalar offset of a buffer load over
+  // the partial slots of the launch, 2 per workgroup; a lane's offset in a
+  // slot is computed once.
+  const __amdgpu_buffer_rsrc_t r_acc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<void*>(p.ws_acc), 0, 2 * int(gridDim.x) * GG * D_PAD * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t r_ml = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<void*>(p.ws_ml), 0, 2 * int(gridDim.x) * GG * 8, kBufferWord3);
   for (int chunk = threadIdx.x; chunk < NCH; chunk += NWAVES * kWaveSize) {
     const int h = (chunk * 4) / D_PAD;
     const int c = (chunk * 4) % D_PAD;
+    const int acc_off = (h * D_PAD + c) * 4;
+    const int ml_off = h * 8;
     float mx = -INFINITY, d = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < n; j0 += UB) {
-      float2 ml[UB], a0[UB], a1[UB];
+      float2 ml[UB];
+      float4 a[UB];
+      // Pieces past the last re-read the last one and get weight 0, so the
+      // batch is issued without branches and consumed on every path (as in
+      // merge_splits).
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        ml[u] = make_float2(-INFINITY, 0.0f);
-        a0[u] = a1[u] = make_float2(0.f, 0.f);
-        if (j0 + u < n) {
-          const int64_t part = part_of(j0 + u, h);
-          ml[u] = fetch2(p.ws_ml + 2 * part);
-          a0[u] = fetch2(p.ws_acc + part * D_PAD + c);
-          a1[u] = fetch2(p.ws_acc + part * D_PAD + c + 2);
-        }
+        const int slot = __builtin_amdgcn_readfirstlane(slot_of(j0 + u < n ? j0 + u : n - 1));
+        const u32x2_t m2 = __builtin_amdgcn_raw_buffer_load_b64(r_ml, ml_off, slot * GG * 8,
+                                                                 kDeviceScopeLoad);
+        const u32x4_t a4 = __builtin_amdgcn_raw_buffer_load_b128(
+            r_acc, acc_off, slot * GG * D_PAD * 4, kDeviceScopeLoad);
+        ml[u] = make_float2(__uint_as_float(m2.x), __uint_as_float(m2.y));
+        a[u] = make_float4(__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
+                           __uint_as_float(a4.w));
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        if (j0 + u >= n) ml[u].x = -INFINITY;
       float m_new = mx;
 #pragma unroll
       for (int u = 0; u < UB; ++u) m_new = fmaxf(m_new, ml[u].x);
-      if (m_new == -INFINITY) continue;
-      const float a = __builtin_amdgcn_exp2f(mx - m_new);
-      d *= a;
-      acc = make_float4(acc.x * a, acc.y * a, acc.z * a, acc.w * a);
+      const float ms = m_new == -INFINITY ? 0.0f : m_new;
+      const float aw = __builtin_amdgcn_exp2f(mx - ms);
+      d *= aw;
+      acc = make_float4(acc.x * aw, acc.y * aw, acc.z * aw, acc.w * aw);
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        const float wu = __builtin_amdgcn_exp2f(ml[u].x - m_new);
+        const float wu = __builtin_amdgcn_exp2f(ml[u].x - ms);
         d = fmaf(wu, ml[u].y, d);
-        acc.x = fmaf(wu, a0[u].x, acc.x);
-        acc.y = fmaf(wu, a0[u].y, acc.y);
-        acc.z = fmaf(wu, a1[u].x, acc.z);
-        acc.w = fmaf(wu, a1[u].y, acc.w);
+        acc.x = fmaf(wu, a[u].x, acc.x);
+        acc.y = fmaf(wu, a[u].y, acc.y);
+        acc.z = fmaf(wu, a[u].z, acc.z);
+        acc.w = fmaf(wu, a[u].w, acc.w);
       }
       mx = m_new;
     }
@@ -1279,9 +1340,7 @@ __attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_deco
 #ifdef NP_TRACE
     sk_stamp(8 + 4 * NP_TRACE_SK_PIECES + 4 * i);
 #endif
-    merge_pieces<DT, D_PAD, HW * G, kSkWaves>(p, ms, mh * HW * G, mn, [&](int j, int h) {
-      return int64_t(slot_of(j)) * (HW * G) + h;
-    });
+    merge_pieces<DT, D_PAD, HW * G, kSkWaves>(p, ms, mh * HW * G, mn, slot_of);
 #ifdef NP_TRACE
     sk_stamp(10 + 4 * NP_TRACE_SK_PIECES + 4 * i);
 #endif
@@ -1307,9 +1366,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams p
   if (L < 1 || L > p.max_blocks * BS || nb > p.max_splits * p.bps) return;
   const int splits = (nb + p.bps - 1) / p.bps;
   if (splits <= 1) return;
-  merge_splits<DT, D_PAD, G>(p, s, kvh, splits, [&](int j, int h) {
-    return (int64_t(s) * p.hq + int64_t(kvh) * G + h) * p.max_splits + j;
-  });
+  merge_splits<DT, D_PAD, G>(p, s, kvh, splits);
 }
 
 template <int DT, int D_PAD, int G>
