@@ -478,9 +478,17 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
 template <int LPR>
 __device__ __forceinline__ float wave_max_rows(float x) {
   if constexpr (LPR <= 8) x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8 (lane i <-> i^8)
-  if constexpr (LPR <= 16)
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(
-                                               __builtin_bit_cast(int, x), 0x401F)));   // i^16
+  if constexpr (LPR <= 16) {
+    // Lanes i and i ^ 16: a gfx950 lane swap of x with itself leaves, in
+    // every lane, one 16-lane group of the pair in each result, so their max
+    // is the pair's. (A VALU op: an LDS swizzle here would make the compiler
+    // wait on the lgkm counter, which also waits for the scalar table reads
+    // of the next group.)
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    x = fmaxf(__uint_as_float(r0), __uint_as_float(r1));
+  }
   const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
   const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
   return fmaxf(lo, hi);
@@ -656,17 +664,22 @@ __device__ __forceinline__ void wave_accumulate(
         }
       }
   };
+  // Every block of a group is loaded, so a group issues the same number of
+  // loads on every path. (A load skipped on one path makes the compiler's
+  // counter wait before a group's use also cover the next group's loads,
+  // which then no longer overlap this group's compute.) A block past this
+  // wave's share reads the same rows of pool block 0, a valid address, and
+  // is masked like any slot past the history.
   auto load_group = [&](const int g0, uint4 (&kr)[NG][NLB], uint4 (&vr)[NG][NLB]) {
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      if (g0 + i < nwb) {
-        const int64_t base =
-            int64_t(bt_row.phys(ph[i], b_first + (g0 + i) * STRIDE)) * p.kv_s0 + head_off;
+      const int64_t blk =
+          g0 + i < nwb ? int64_t(bt_row.phys(ph[i], b_first + (g0 + i) * STRIDE)) : 0;
+      const int64_t base = blk * p.kv_s0 + head_off;
 #pragma unroll
-        for (int j = 0; j < NLB; ++j) {
-          kr[i][j] = load16_stream(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
-          vr[i][j] = load16_stream(p.v, base + int64_t(j * TPL) * p.kv_s1, kElt);
-        }
+      for (int j = 0; j < NLB; ++j) {
+        kr[i][j] = load16_stream(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
+        vr[i][j] = load16_stream(p.v, base + int64_t(j * TPL) * p.kv_s1, kElt);
       }
     }
     // Table entries of the group after the one just issued.
@@ -679,17 +692,28 @@ __device__ __forceinline__ void wave_accumulate(
     }
   };
 
-  // Software pipeline over groups with two register buffers: the loads of
-  // group g + 1 are in flight while group g computes.
+  // Software pipeline over the ngr groups with two register buffers: the
+  // loads of group g + 1 are in flight while group g computes. No load is
+  // issued conditionally between a group's loads and its use, so every wait
+  // before a group's compute leaves the next group's loads in flight; past
+  // the last group the loop loads one group of pool block 0 (all masked,
+  // never computed) instead of skipping the loads.
+  const int ngr = nwb > 0 ? (nwb + NG - 1) / NG : 0;
   uint4 ka[NG][NLB], va[NG][NLB], kb[NG][NLB], vb[NG][NLB];
-  if (nwb > 0) load_group(0, ka, va);
-  for (int g0 = 0; g0 < nwb; g0 += 2 * NG) {
-    if (g0 + NG < nwb) load_group(g0 + NG, kb, vb);
-    if (stamps != nullptr && g0 == 0) stamps->at(2);
-    compute_group(g0, ka, va);
-    if (g0 + NG >= nwb) break;
-    if (g0 + 2 * NG < nwb) load_group(g0 + 2 * NG, ka, va);
-    compute_group(g0 + NG, kb, vb);
+  if (ngr == 1) {
+    load_group(0, ka, va);
+    if (stamps != nullptr) stamps->at(2);
+    compute_group(0, ka, va);
+  } else if (ngr > 1) {
+    load_group(0, ka, va);
+    for (int g = 0; g < ngr; g += 2) {
+      load_group((g + 1) * NG, kb, vb);
+      if (stamps != nullptr && g == 0) stamps->at(2);
+      compute_group(g * NG, ka, va);
+      if (g + 1 >= ngr) break;
+      load_group((g + 2) * NG, ka, va);
+      compute_group((g + 1) * NG, kb, vb);
+    }
   }
 
 }
@@ -999,15 +1023,6 @@ __global__ __launch_bounds__(kDecodeWaves * kWaveSize) void paged_decode_kernel(
 // the schedule always matches the lengths the kernel reads and the workspace
 // bounds depend only on W.
 
-// Waves per SIMD the stream-K kernel is compiled for: three where the
-// registers allow it without spilling (head_dim 64 with up to 4 heads per
-// group, 16-bit head_dim 128 with up to 3), else no constraint. The planner's
-// default, one 8-wave workgroup per CU, needs two; the tighter register limit
-// measured no slower.
-constexpr int sk_min_waves(int dt, int d_pad, int g) {
-  return (d_pad == 64 && g <= 4) || (d_pad == 128 && dt != NP_F32 && g <= 3) ? 3 : 1;
-}
-
 // Merge of the n pieces of one segment, GG query heads from head0: every
 // thread owns float4 chunks of the GG x d_pad output and folds in all pieces
 // (UB loads in flight at a time), with the split-KV page's log-sum-exp
@@ -1079,9 +1094,10 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int h
   }
 }
 
+// The 8-wave workgroup (launch bounds) allows up to 256 VGPRs per lane, two
+// waves per SIMD: the planner's default of one workgroup per CU.
 template <int DT, int D_PAD, int G, int BS, int HW>
-__global__ __launch_bounds__(kSkWaves * kWaveSize)
-__attribute__((amdgpu_waves_per_eu(sk_min_waves(DT, D_PAD, G)))) void paged_decode_sk_kernel(
+__global__ __launch_bounds__(kSkWaves * kWaveSize) void paged_decode_sk_kernel(
     const DecodeParams p) {
   using S = DecodeShape<DT, D_PAD, BS, kSkWaves>;
   constexpr int kElt = S::kElt, VEC = S::VEC, LPR = S::LPR, NG = S::NG, NW = S::NW;
