@@ -664,22 +664,29 @@ __device__ __forceinline__ void wave_accumulate(
         }
       }
   };
-  // Every block of a group is loaded, so a group issues the same number of
-  // loads on every path. (A load skipped on one path makes the compiler's
-  // counter wait before a group's use also cover the next group's loads,
-  // which then no longer overlap this group's compute.) A block past this
-  // wave's share reads the same rows of pool block 0, a valid address, and
-  // is masked like any slot past the history.
-  auto load_group = [&](const int g0, uint4 (&kr)[NG][NLB], uint4 (&vr)[NG][NLB]) {
+  // In the pipeline (every_block) every block of a group is loaded, so a
+  // group issues the same number of loads on every path. (A load skipped on
+  // one path makes the compiler's counter wait before a group's use also
+  // cover the next group's loads, which then no longer overlap this group's
+  // compute.) Every lane then reads the first 16 bytes of the pool for a
+  // block past this wave's share (one line, so the load costs one request),
+  // and the block is masked like any slot past the history. A wave with a
+  // single group has nothing to overlap and skips such blocks.
+  auto load_group = [&](const int g0, uint4 (&kr)[NG][NLB], uint4 (&vr)[NG][NLB],
+                        const bool every_block) {
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int64_t blk =
-          g0 + i < nwb ? int64_t(bt_row.phys(ph[i], b_first + (g0 + i) * STRIDE)) : 0;
-      const int64_t base = blk * p.kv_s0 + head_off;
+      const bool real = g0 + i < nwb;
+      if (every_block || real) {
+        const int64_t base =
+            real ? int64_t(bt_row.phys(ph[i], b_first + (g0 + i) * STRIDE)) * p.kv_s0 + head_off
+                 : 0;
+        const int64_t step = real ? int64_t(TPL) * p.kv_s1 : 0;
 #pragma unroll
-      for (int j = 0; j < NLB; ++j) {
-        kr[i][j] = load16_stream(p.k, base + int64_t(j * TPL) * p.kv_s1, kElt);
-        vr[i][j] = load16_stream(p.v, base + int64_t(j * TPL) * p.kv_s1, kElt);
+        for (int j = 0; j < NLB; ++j) {
+          kr[i][j] = load16_stream(p.k, base + j * step, kElt);
+          vr[i][j] = load16_stream(p.v, base + j * step, kElt);
+        }
       }
     }
     // Table entries of the group after the one just issued.
@@ -696,22 +703,22 @@ __device__ __forceinline__ void wave_accumulate(
   // loads of group g + 1 are in flight while group g computes. No load is
   // issued conditionally between a group's loads and its use, so every wait
   // before a group's compute leaves the next group's loads in flight; past
-  // the last group the loop loads one group of pool block 0 (all masked,
-  // never computed) instead of skipping the loads.
+  // the last group the loop issues one group of stand-in loads (never
+  // computed) instead of skipping the loads.
   const int ngr = nwb > 0 ? (nwb + NG - 1) / NG : 0;
   uint4 ka[NG][NLB], va[NG][NLB], kb[NG][NLB], vb[NG][NLB];
   if (ngr == 1) {
-    load_group(0, ka, va);
+    load_group(0, ka, va, false);
     if (stamps != nullptr) stamps->at(2);
     compute_group(0, ka, va);
   } else if (ngr > 1) {
-    load_group(0, ka, va);
+    load_group(0, ka, va, true);
     for (int g = 0; g < ngr; g += 2) {
-      load_group((g + 1) * NG, kb, vb);
+      load_group((g + 1) * NG, kb, vb, true);
       if (stamps != nullptr && g == 0) stamps->at(2);
       compute_group(g * NG, ka, va);
       if (g + 1 >= ngr) break;
-      load_group((g + 2) * NG, ka, va);
+      load_group((g + 2) * NG, ka, va, true);
       compute_group((g + 1) * NG, kb, vb);
     }
   }
