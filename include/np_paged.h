@@ -115,7 +115,10 @@ typedef struct np_plan_opts {
   int32_t wgs_per_cu;             /* target workgroups per CU; 0 => 1          */
   int32_t min_blocks_per_split;   /* 0 => 4 (uniform); stream-K: least units
                                      per workgroup, 0 => 8                     */
-  int32_t max_blocks_per_split;   /* 0 => 1024 tokens' worth of blocks         */
+  int32_t max_blocks_per_split;   /* uniform splits; 0 => no cap for equal
+                                     lengths (the split fills the CUs once),
+                                     1024 tokens' worth of blocks when the
+                                     longest sequence has over 1.25x the mean */
   int32_t force_blocks_per_split; /* > 0: use exactly this split size          */
   int32_t combine_mode;           /* 0: the last split workgroup of each
                                      (sequence, KV head) merges the splits in

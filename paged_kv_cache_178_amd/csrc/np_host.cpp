@@ -314,9 +314,6 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
   const int32_t num_cus = o.num_cus ? o.num_cus : 256;
   const int32_t wgs_per_cu = o.wgs_per_cu ? o.wgs_per_cu : 1;
   const int32_t min_bps = o.min_blocks_per_split ? o.min_blocks_per_split : 4;
-  const int32_t max_bps = o.max_blocks_per_split
-                              ? o.max_blocks_per_split
-                              : std::max<int32_t>(1, 1024 / desc->block_size);
 
   np_plan_s* plan = new (std::nothrow) np_plan_s();
   if (plan == nullptr) return NP_ERR_UNSUPPORTED;
@@ -387,6 +384,16 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
       total_blocks += nb;
       max_nb = std::max(max_nb, nb);
     }
+    // A split's blocks stream as one pipelined range, so for equal lengths
+    // the best split size fills the CUs once (measured from 4 to 128 Ki
+    // tokens). When the lengths are ragged (the longest over 1.25x the mean)
+    // smaller splits, 1024 tokens' worth by default, keep the longest
+    // sequences from forming a tail.
+    const bool ragged = max_nb * 4 * c.num_seqs > total_blocks * 5;
+    const int64_t max_bps =
+        o.max_blocks_per_split ? o.max_blocks_per_split
+        : ragged               ? std::max<int64_t>(1, 1024 / desc->block_size)
+                               : std::max<int64_t>(max_nb, 1);
     int64_t bps;
     if (o.force_blocks_per_split > 0) {
       bps = o.force_blocks_per_split;
@@ -394,7 +401,7 @@ np_status np_plan(const np_paged_desc* desc, const int32_t* lens, const int32_t*
       const int64_t target_wgs = int64_t(num_cus) * wgs_per_cu;
       bps = ceil_div(total_blocks * c.hkv, target_wgs);
       bps = std::max<int64_t>(bps, min_bps);
-      bps = std::min<int64_t>(bps, std::max(max_bps, min_bps));
+      bps = std::min<int64_t>(bps, std::max<int64_t>(max_bps, min_bps));
     }
     bps = std::min<int64_t>(bps, std::max<int64_t>(max_nb, 1));
     c.schedule = kScheduleUniform;

@@ -142,8 +142,10 @@ def test_check_errors():
 def model_decode_plan(lens, bs, hkv, num_cus=256, wgs_per_cu=1, min_bps=4, max_bps=None,
                       force=0):
     """Brute-force statement of the decode plan rule."""
-    max_bps = max_bps or max(1, 1024 // bs)
     nbs = [math.ceil(x / bs) for x in lens]
+    if not max_bps:
+        ragged = max(nbs) * 4 * len(nbs) > sum(nbs) * 5
+        max_bps = max(1, 1024 // bs) if ragged else max(max(nbs), 1)
     if force:
         bps = force
     else:
