@@ -357,6 +357,15 @@ def test_decode_plan_named_workloads():
     d = desc(num_seqs=1, hq=32, hkv=8, max_blocks=256, n_blocks=512)
     p = B.np_plan(d, np.array([4096], np.int32))
     assert p.blocks_per_split == 8 and p.max_splits == 32
+    # Equal lengths fill the CUs once with no cap: 131072 tokens, 8192 blocks x 8
+    # KV heads over 256 workgroups (the ragged-batch cap would give 64 blocks).
+    d = desc(num_seqs=1, hq=32, hkv=8, max_blocks=8192, n_blocks=8192)
+    p = B.np_plan(d, np.array([131072], np.int32))
+    assert p.blocks_per_split == 256 and p.max_splits == 32
+    # The contiguous split-KV workload at 16384 tokens: 4 x 1024 blocks x 16 heads.
+    d = desc(num_seqs=4, hq=16, hkv=16, max_blocks=1024, n_blocks=4096)
+    p = B.np_plan(d, np.full(4, 16384, np.int32))
+    assert p.blocks_per_split == 256 and p.max_splits == 4
     # Continuous batching: sequences up to 1024 tokens stay unsplit.
     rng = np.random.default_rng(4)
     lens = rng.integers(128, 8192, size=64, endpoint=True).astype(np.int32)
