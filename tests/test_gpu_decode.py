@@ -213,9 +213,28 @@ def test_edge_lengths(lens):
 
 @pytest.mark.parametrize("opts", [dict(), dict(schedule=2)], ids=["uniform", "stream_k"])
 def test_long_history_32k(opts):
-    """A 32768-token history (2048 blocks, 64 splits of the default plan)."""
+    """A 32768-token history (2048 blocks; the default plan cuts it into 32
+    splits of 64 blocks, one workgroup per CU)."""
     _run_parity(wl.custom(46, [32768], hq=32, hkv=8, d=64, dtype="bf16"),
                 binding.PlanOpts(**opts))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Seeded random shapes across dtype, head_dim, group size, ragged lengths,
+    schedule and forced split size: partial last groups, waves with one or many
+    groups, and both merge paths."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f16", "f32"][seed % 3]
+    d = int(rng.choice([48, 64, 96, 128]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 8]))
+    n = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(1, 6000, size=n)]
+    inp = wl.custom(200 + seed, lens, hq=hkv * group, hkv=hkv, d=d, dtype=dtype)
+    opts = [dict(), dict(schedule=1), dict(schedule=2),
+            dict(force_blocks_per_split=int(rng.integers(1, 40)))][seed % 4]
+    _run_parity(inp, binding.PlanOpts(**opts))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
