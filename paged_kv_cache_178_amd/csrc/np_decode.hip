@@ -295,10 +295,12 @@ __device__ __forceinline__ uint4 load16(const void* base, int64_t elem_off, int 
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem_off * elt);
 }
 
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+
 // K/V rows are read exactly once per call: a nontemporal (streaming) load
 // keeps them from displacing reusable lines.
 __device__ __forceinline__ uint4 load16_stream(const void* base, int64_t elem_off, int elt) {
-  typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
   const u32x4_t v = __builtin_nontemporal_load(
       reinterpret_cast<const u32x4_t*>(static_cast<const char*>(base) + elem_off * elt));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -326,9 +328,6 @@ constexpr int kBufferWord3 = 0x00020000;
 // agent-scope stores: the device-scope bit (sc1), the same bit an agent-scope
 // atomic load carries.
 constexpr int kDeviceScopeLoad = 16;
-
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 
 // Merge the splits of one (sequence, KV head): with M = max_j m_j,
 // out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j. This is the split-KV
