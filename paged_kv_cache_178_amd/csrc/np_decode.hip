@@ -336,7 +336,8 @@ constexpr int kDeviceScopeLoad = 16;
 //
 // Latency-parallel: waves take splits round-robin, each lane owns float4
 // chunks of the G x d_pad output, and a batch of UB splits has all its loads
-// in flight before any is used; the per-wave states are merged through LDS.
+// in flight before any is used (one 16-byte acc load per split and chunk, one
+// (m, l) load per wave); the per-wave states are merged through LDS.
 // The partials of query head kvh * G + h and split j sit at part
 // row0 + h * max_splits + j. Each lane's offset inside the head group's rows
 // is computed once; a split moves every lane by the same amount, which is a
@@ -359,16 +360,25 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
       static_cast<void*>(p.ws_acc + row0 * D_PAD), 0, G * p.max_splits * D_PAD * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t r_ml = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<void*>(p.ws_ml + 2 * row0), 0, G * p.max_splits * 8, kBufferWord3);
-  int acc_off[CPL], ml_off[CPL];
+  int acc_off[CPL], hd[CPL];
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) {
     // Lanes past the output re-read its last chunk and get weight 0.
     const int chunk = lane + ci * kWaveSize;
     const int cc = chunk < NCH ? chunk : NCH - 1;
-    const int h = (cc * 4) / D_PAD;
-    acc_off[ci] = (h * p.max_splits * D_PAD + (cc * 4) % D_PAD) * 4;
-    ml_off[ci] = h * p.max_splits * 8;
+    hd[ci] = (cc * 4) / D_PAD;
+    acc_off[ci] = (hd[ci] * p.max_splits * D_PAD + (cc * 4) % D_PAD) * 4;
   }
+  // The (m, l) pairs of a batch: lane u * G + h of a wave loads split u's
+  // pair of head h (UB * G <= 64 lanes), and every lane reads the pairs of
+  // its chunks' heads back from the wave's LDS row. A full-width load costs
+  // the CU's address unit about the same whatever it reads, and the time to
+  // issue the batch is what the merge waits on, so one load here instead of
+  // UB per lane shortens it.
+  static_assert(UB * G <= kWaveSize, "a batch's (m, l) pairs fit one wave");
+  __shared__ float2 s_mlb[NW][kWaveSize];
+  const int pl = lane < UB * G ? lane : UB * G - 1;
+  const int pu = pl / G, phd = pl % G;
 
   float mw[CPL], dw[CPL];
   float4 nw[CPL];
@@ -381,18 +391,18 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
   for (int j0 = wave; j0 < splits; j0 += NW * UB) {
     float2 ml[UB][CPL];
     float4 a[UB][CPL];
+    // A split past the last re-reads the last one and gets weight 0, so the
+    // batch is issued without branches.
+    const int jp = j0 + pu * NW < splits ? j0 + pu * NW : splits - 1;
+    const u32x2_t mp = __builtin_amdgcn_raw_buffer_load_b64(
+        r_ml, (phd * p.max_splits + jp) * 8, 0, kDeviceScopeLoad);
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
-      // A split past the last re-reads the last one and gets weight 0, so
-      // the batch is issued without branches.
       const int j = j0 + u * NW < splits ? j0 + u * NW : splits - 1;
 #pragma unroll
       for (int ci = 0; ci < CPL; ++ci) {
-        const u32x2_t m2 = __builtin_amdgcn_raw_buffer_load_b64(r_ml, ml_off[ci], j * 8,
-                                                                 kDeviceScopeLoad);
         const u32x4_t a4 = __builtin_amdgcn_raw_buffer_load_b128(r_acc, acc_off[ci],
                                                                   j * D_PAD * 4, kDeviceScopeLoad);
-        ml[u][ci] = make_float2(__uint_as_float(m2.x), __uint_as_float(m2.y));
         a[u][ci] = make_float4(__uint_as_float(a4.x), __uint_as_float(a4.y),
                                __uint_as_float(a4.z), __uint_as_float(a4.w));
       }
@@ -401,6 +411,13 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int s, int k
     // the scheduler may sink the last split's loads below the maximum, which
     // costs one more memory round trip.
     __builtin_amdgcn_sched_barrier(0);
+    // (The row is the wave's own: its lanes write and read it in program
+    // order, which LDS keeps, so no barrier.)
+    s_mlb[wave][lane] = make_float2(__uint_as_float(mp.x), __uint_as_float(mp.y));
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+#pragma unroll
+      for (int ci = 0; ci < CPL; ++ci) ml[u][ci] = s_mlb[wave][u * G + hd[ci]];
 #pragma unroll
     for (int u = 0; u < UB; ++u)
 #pragma unroll
