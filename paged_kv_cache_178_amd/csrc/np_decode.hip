@@ -1064,6 +1064,14 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int h
       static_cast<void*>(p.ws_acc), 0, 2 * int(gridDim.x) * GG * D_PAD * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t r_ml = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<void*>(p.ws_ml), 0, 2 * int(gridDim.x) * GG * 8, kBufferWord3);
+  // As in merge_splits, when a batch's (m, l) pairs fit one wave (UB * GG <=
+  // 64), lane u * GG + h loads piece u's pair of head h once and the lanes
+  // read theirs from the wave's LDS row; otherwise every lane loads its own.
+  constexpr bool kShareMl = UB * GG <= kWaveSize;
+  __shared__ float2 s_mlp[NWAVES][kWaveSize];
+  const int wv = threadIdx.x / kWaveSize, ln = threadIdx.x % kWaveSize;
+  const int pl = ln < UB * GG ? ln : UB * GG - 1;
+  const int pu = pl / GG, phd = pl % GG;
   for (int chunk = threadIdx.x; chunk < NCH; chunk += NWAVES * kWaveSize) {
     const int h = (chunk * 4) / D_PAD;
     const int c = (chunk * 4) % D_PAD;
@@ -1077,18 +1085,29 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int s, int h
       // Pieces past the last re-read the last one and get weight 0, so the
       // batch is issued without branches and consumed on every path (as in
       // merge_splits).
+      u32x2_t mp = {0u, 0u};
+      if constexpr (kShareMl)
+        mp = __builtin_amdgcn_raw_buffer_load_b64(
+            r_ml, (slot_of(j0 + pu < n ? j0 + pu : n - 1) * GG + phd) * 8, 0, kDeviceScopeLoad);
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int slot = __builtin_amdgcn_readfirstlane(slot_of(j0 + u < n ? j0 + u : n - 1));
-        const u32x2_t m2 = __builtin_amdgcn_raw_buffer_load_b64(r_ml, ml_off, slot * GG * 8,
-                                                                 kDeviceScopeLoad);
+        if constexpr (!kShareMl) {
+          const u32x2_t m2 = __builtin_amdgcn_raw_buffer_load_b64(r_ml, ml_off, slot * GG * 8,
+                                                                   kDeviceScopeLoad);
+          ml[u] = make_float2(__uint_as_float(m2.x), __uint_as_float(m2.y));
+        }
         const u32x4_t a4 = __builtin_amdgcn_raw_buffer_load_b128(
             r_acc, acc_off, slot * GG * D_PAD * 4, kDeviceScopeLoad);
-        ml[u] = make_float2(__uint_as_float(m2.x), __uint_as_float(m2.y));
         a[u] = make_float4(__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
                            __uint_as_float(a4.w));
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kShareMl) {
+        s_mlp[wv][ln] = make_float2(__uint_as_float(mp.x), __uint_as_float(mp.y));
+#pragma unroll
+        for (int u = 0; u < UB; ++u) ml[u] = s_mlp[wv][u * GG + h];
+      }
 #pragma unroll
       for (int u = 0; u < UB; ++u)
         if (j0 + u >= n) ml[u].x = -INFINITY;
