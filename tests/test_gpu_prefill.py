@@ -5,6 +5,7 @@ past + i, past = context_len - n_q, and sees keys t <= past + i. Tolerance
 atol = rtol = 1e-2 (bf16/fp16 inputs), element by element.
 """
 
+import numpy as np
 import pytest
 import torch
 
@@ -34,6 +35,25 @@ def test_chunked_prefill_full_size():
 ])
 def test_ragged_chunks(lens, n_q):
     _run(wl.custom(50 + len(lens) + sum(n_q), lens, n_q=n_q, hq=8, hkv=2, d=64, dtype="bf16"))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_chunks(seed):
+    """Seeded random chunks: 1-4 sequences, past lengths 0-3000 (a fifth of them
+    with no past), chunks of 1-300 rows, group sizes 1-8 and both input types,
+    with K spikes on every other seed; so query tiles end mid-unit, key tiles end
+    mid-block, wave groups start on tiles some rows cannot see, and workgroups
+    carry idle units."""
+    rng = np.random.default_rng(3000 + seed)
+    dtype = ["bf16", "f16"][seed % 2]
+    group = int(rng.choice([1, 2, 3, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4]))
+    n = int(rng.integers(1, 5))
+    n_q = [int(x) for x in rng.integers(1, 301, size=n)]
+    past = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(0, 3001, size=n)]
+    lens = [a + b for a, b in zip(past, n_q)]
+    _run(wl.custom(400 + seed, lens, n_q=n_q, hq=hkv * group, hkv=hkv, d=64, dtype=dtype,
+                   spike_frac=0.01 if seed % 2 else 0.0))
 
 
 @pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 8])
