@@ -138,9 +138,12 @@ __device__ __forceinline__ float sum_pairs(const uint4& x, float l) {
 
 // Scores are finite or -inf here (masked slots are set to -inf by index
 // before any max), so this file is built without NaN semantics and the max
-// needs no canonicalisation (it becomes v_max3_f32).
+// needs no canonicalisation: max(max(a, b), c) becomes one v_max3_f32. The
+// running value goes first, so that a chain max3(m, x, y), max3(m', x', y')
+// takes one instruction per two values (with the running value innermost on
+// the other side, each pair of new values becomes a v_max_f32 of its own).
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  return fmaxf(a, fmaxf(b, c));
+  return fmaxf(fmaxf(a, b), c);
 }
 
 __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off) {
@@ -334,11 +337,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
         for (int i = 0; i < 16; ++i)
           st[b][i] = 32 * b + 8 * (i / 4) + (i % 4) <= lim ? st[b][i] : -INFINITY;
     }
-    float mxr = max3(st[0][0], st[1][0], st[0][1]);
-    mxr = max3(mxr, st[1][1], st[0][2]);
+    // Two chains of 7 (one per 32-key half), then 2 more: 16 instructions.
+    float ma = max3(st[0][0], st[0][1], st[0][2]);
+    float mb = max3(st[1][0], st[1][1], st[1][2]);
 #pragma unroll
-    for (int i = 2; i < 15; ++i) mxr = max3(mxr, st[1][i], st[0][i + 1]);
-    mxr = max3(mxr, st[1][15], st[1][15]);
+    for (int i = 3; i < 15; i += 2) {
+      ma = max3(ma, st[0][i], st[0][i + 1]);
+      mb = max3(mb, st[1][i], st[1][i + 1]);
+    }
+    const float mxr = max3(ma, mb, max3(st[0][15], st[1][15], st[1][15]));
     if (__ballot(mxr * c > m[qb] + kLazy)) {
       const float mx = fmaxf(mxr, __shfl_xor(mxr, 32)) * c;   // same for the lane pair
       const bool move = mx > m[qb] + kLazy;                   // first tile: m = -inf
