@@ -242,7 +242,13 @@ def cache_flush() -> None:
 
 def graph_us(fn, n: int) -> float:
     """Average device time per call of n calls captured in one HIP graph: one
-    untimed replay, a 512 MiB cache flush, then the timed replay."""
+    untimed replay, a 512 MiB cache flush, then the timed replay.
+
+    The timed replay is enqueued while the flush still runs, so its first
+    kernel starts as soon as the flush ends: the host's submission of the
+    graph (tens of microseconds, paid once per replay however many steps it
+    holds) is not inside the interval, and the time per step does not depend
+    on n."""
     import torch
 
     graph = torch.cuda.CUDAGraph()
@@ -253,8 +259,8 @@ def graph_us(fn, n: int) -> float:
             fn(i)
     torch.cuda.synchronize()
     graph.replay()
-    cache_flush()
     torch.cuda.synchronize()
+    cache_flush()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
