@@ -307,12 +307,19 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
 
-  const float c = p.scale_log2;
+  const float c = p.scale_log2;   // > 0
+  const float rc = 1.0f / c;
   float m[QB], l[QB];          // running reference max (scaled, log2 units); lane's half-sum
+  // Kept beside m, updated only when m moves: the exponent offset of the
+  // weights (-m, or 0 while m is -inf) and the raw score above which m moves,
+  // (m + kLazy) / c, so that neither costs instructions per tile.
+  float nm[QB], thr[QB];
   f32x16_t acc[QB][kD / 32];   // O^T column blocks
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -INFINITY;
+    nm[qb] = 0.0f;
+    thr[qb] = -INFINITY;
     l[qb] = 0.0f;
 #pragma unroll
     for (int cb = 0; cb < kD / 32; ++cb) acc[qb][cb] = f32x16_t{};
@@ -346,11 +353,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
       mb = max3(mb, st[1][i], st[1][i + 1]);
     }
     const float mxr = max3(ma, mb, max3(st[0][15], st[1][15], st[1][15]));
-    if (__ballot(mxr * c > m[qb] + kLazy)) {
+    if (__ballot(mxr > thr[qb])) {
       const float mx = fmaxf(mxr, __shfl_xor(mxr, 32)) * c;   // same for the lane pair
       const bool move = mx > m[qb] + kLazy;                   // first tile: m = -inf
       const float alpha = move ? __builtin_amdgcn_exp2f(m[qb] - mx) : 1.0f;
       m[qb] = move ? mx : m[qb];
+      nm[qb] = move ? -mx : nm[qb];
+      thr[qb] = move ? (mx + kLazy) * rc : thr[qb];
       l[qb] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < kD / 32; ++cb)
@@ -362,10 +371,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void paged_prefill_kerne
   // registers 8(ks%2) .. 8(ks%2)+7 of half ks/2. The row sum adds the same
   // rounded weights the product uses (v_dot2 against (1, 1)).
   // A lane whose scores so far were all masked still has m = -inf (a wave
-  // group may start on a tile that some of its rows cannot see): its weights
-  // must be 0, not exp2(-inf + inf).
+  // group may start on a tile that some of its rows cannot see): its offset
+  // nm is 0, so its weights are 0, not exp2(-inf + inf).
   auto weights = [&](int qb, int ks, const f32x16_t (&st)[2], uint4 (&pb)[4]) __attribute__((always_inline)) {
-    const float neg_m = m[qb] == -INFINITY ? 0.0f : -m[qb];
+    const float neg_m = nm[qb];
     float e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
