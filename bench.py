@@ -18,7 +18,10 @@ touched, twice the 256 MiB Infinity Cache: cold HBM at any K.
 Printed: one JSON line with KV GB/s (whole job), microseconds per step, the
 decode kernel's roofline against 8 TB/s HBM and the float64 oracle's
 throughput on this host's cores. Before any timing the GPU output is checked
-against the oracle (atol = rtol = 1e-2).
+against the oracle (atol = rtol = 1e-2). The same line carries, under
+"secondary", the continuous-batching decode and the chunked prefill below,
+each measured by a child run of this script with its default steps and
+warmup (--no-secondary leaves them out).
 
 Other workloads (not the headline, one JSON line each):
   --workload batching  64 sequences, lengths uniform on [128, 8192], Llama head
@@ -42,6 +45,7 @@ import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -135,6 +139,8 @@ def parse_args(argv=None):
                     help="stream-K: fixed cost of a (sequence, KV head) in blocks (0: default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="headline only: skip the batching and prefill child runs")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for hardware counters: a few decode steps and a plain "
                          "256 MiB copy, no timing")
@@ -519,8 +525,44 @@ def main(argv=None) -> int:
                                          one_thread_gbs=round(rate(kv_bytes, best1 * 1e6), 4))
     else:
         rec["cpu_baseline"] = None
+    if args.history == 4096 and not args.warm and not args.no_secondary:
+        rec["secondary"] = secondary_runs()
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def secondary_runs(workloads=("batching", "prefill")) -> dict:
+    """The continuous-batching decode and the chunked prefill, each measured by a
+    child run of this script (default plan, parity gate, graph timing, no CPU
+    leg, default steps and warmup, so the per-replay graph overhead is spread
+    as in their own runs). A child that fails is recorded with its exit
+    status; the headline line is printed either way."""
+    out = {}
+    for w in workloads:
+        log(f"[bench] secondary workload {w}: child run")
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--no-cpu-baseline"]
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        except subprocess.TimeoutExpired:
+            out[w] = {"error": "child run timed out after 600 s"}
+            continue
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            out[w] = {"error": f"child run exited with status {r.returncode}",
+                      "stderr_tail": r.stderr[-400:]}
+            continue
+        child = json.loads(lines[-1])
+        out[w] = {
+            "metric": child["metric"], "value": child["value"], "unit": child["unit"],
+            "us_per_step": child["us_per_step"], "steps": child["steps"],
+            "roofline_frac": child["roofline"]["frac"], "roofline_bound": child["roofline"]["bound"],
+            "traffic": child["roofline"]["traffic"],
+            "parity_max_abs_err": child["parity_max_abs_err"],
+            "workload": child["config"]["workload"],
+        }
+        log(f"[bench] secondary {w}: {child['us_per_step']} us/step, "
+            f"{child['value']} {child['unit']}")
+    return out
 
 
 SMALL_DECODE = {
