@@ -178,7 +178,7 @@ np_status np_check_paged_inputs(const np_paged_desc* desc, const void* q,
  * (num_cus * wgs_per_cu)), min, max), or the forced value.
  * Decode, stream-K schedule (for batches of ragged lengths; the same
  * partition into page-aligned pieces, cut for equal work instead of equal
- * size): a workgroup serves HW KV heads together (HW = 4, 2 or 1, the largest
+ * size): a workgroup serves HW KV heads together (HW = 8, 4, 2 or 1, the largest
  * dividing Hkv); each (sequence, head group) is a segment of
  * ceil(L/block_size) blocks plus segment_cost virtual units; segments are
  * laid end to end in (sequence, head group) order, U units in all, and

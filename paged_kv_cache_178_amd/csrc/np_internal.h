@@ -32,7 +32,9 @@ constexpr int kTraceStamps = NP_TRACE_STAMPS;  // trace build: phase stamps per 
 
 // Stream-K: KV heads one decode workgroup serves (the largest of 4, 2, 1 that
 // divides Hkv).
-constexpr int sk_heads_per_wg(int hkv) { return hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1; }
+constexpr int sk_heads_per_wg(int hkv) {
+  return hkv % 8 == 0 ? 8 : hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
+}
 
 // Sizes every launch depends on, fixed when the plan is made.
 struct np_plan_core {

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 
 def heads_per_wg(hkv: int) -> int:
-    return 4 if hkv % 4 == 0 else 2 if hkv % 2 == 0 else 1
+    return 8 if hkv % 8 == 0 else 4 if hkv % 4 == 0 else 2 if hkv % 2 == 0 else 1
 
 
 def emulate(lens, bs: int, hkv: int, max_blocks: int, cost: int, W: int):

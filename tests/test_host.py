@@ -231,7 +231,7 @@ def model_stream_k_plan(lens, bs, hkv, max_blocks, cost=4, num_cus=256, per_cu=1
     dividing Hkv); segments are (sequence, head group); intersect every
     workgroup's unit range with every segment's block range. A piece is
     listed once per head of its group."""
-    hw = 4 if hkv % 4 == 0 else 2 if hkv % 2 == 0 else 1
+    hw = 8 if hkv % 8 == 0 else 4 if hkv % 4 == 0 else 2 if hkv % 2 == 0 else 1
     nbs = [min(-(-x // bs), max_blocks) for x in lens]
     segs, start = [], 0
     for s, nb in enumerate(nbs):
