@@ -74,11 +74,18 @@ SK_CASES = [dict(num_cus=1, wgs_per_cu=1),
             dict()]
 
 
-@pytest.mark.parametrize("case", list(range(len(SK_CASES))) + ["batching"],
-                         ids=["one_wg", "unit_per_wg", "virtual_only", "auto", "batching"])
+@pytest.mark.parametrize("case", list(range(len(SK_CASES))) + ["batching", "hkv4", "hkv2"],
+                         ids=["one_wg", "unit_per_wg", "virtual_only", "auto", "batching",
+                              "four_heads_per_wg", "two_heads_per_wg"])
 def test_stream_k_trace_matches_plan(case):
+    lens = [1, 16, 17, 900, 4096, 33, 2000, 15]
     if case == "batching":
         inp, shape = wl.continuous_batching(), {}
+    elif case == "hkv4":     # a workgroup serves 4 KV heads
+        inp, shape = wl.custom(43, lens, hq=16, hkv=4, d=64, dtype="bf16"), {}
+    elif case == "hkv2":     # 2 KV heads, many small pieces
+        inp = wl.custom(44, lens, hq=8, hkv=2, d=64, dtype="bf16")
+        shape = SK_CASES[2]
     else:
         inp = wl.custom(41, [1, 16, 17, 900, 4096, 33, 2000, 15], hq=32, hkv=8, d=64,
                         dtype="bf16")
